@@ -1,0 +1,195 @@
+"""CPU oracle of the routed-experts layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import this
+package. The GPU library never calls it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double precision, optional bf16 storage
+points); this module builds it with gcc and marshals numpy arrays. See the header of
+``moe_oracle.c`` for the definition it follows and the passages it cites.
+
+Modes:
+  * ``"bf16"``  -- inputs are bf16 bit patterns; every storage point of the layer is rounded to bf16.
+                  This is the contract the GPU path is compared against.
+  * ``"exact"`` -- no rounding anywhere; inputs may be bf16 bits or float64 arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+IN_BF16, IN_F64 = 0, 1
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("K", ctypes.c_int64), ("round_bf16", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32)]
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into liboracle.so (gcc -O2 -fopenmp, no fast-math)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-Wno-unused-parameter", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            S = ctypes.POINTER(_Shape)
+            L.oracle_round_bf16.restype = ctypes.c_double
+            L.oracle_round_bf16.argtypes = [ctypes.c_double]
+            L.oracle_plan.restype = I64
+            L.oracle_plan.argtypes = [I64, I64, I64, P, P, P, P, P]
+            L.oracle_forward.restype = ctypes.c_int
+            L.oracle_forward.argtypes = [S] + [P] * 12
+            L.oracle_backward.restype = ctypes.c_int
+            L.oracle_backward.argtypes = [S] + [P] * 19
+            L.oracle_tokens.restype = ctypes.c_int
+            L.oracle_tokens.argtypes = [S, P, P, P, P, P, P, I64, P, P, P, P, P]
+            L.oracle_wgrad_entries.restype = ctypes.c_int
+            L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P]
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shape(T, D, F, E, K, mode, in_dtype):
+    if mode not in ("bf16", "exact"):
+        raise ValueError(mode)
+    return _Shape(T, D, F, E, K, 1 if mode == "bf16" else 0, in_dtype)
+
+
+def _as_input(a, in_dtype):
+    if a is None:
+        return None
+    if in_dtype == IN_BF16:
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 inputs are passed as uint16 bit patterns")
+        return np.ascontiguousarray(a)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _in_dtype_of(x):
+    return IN_BF16 if x.dtype == np.uint16 else IN_F64
+
+
+def round_bf16(v: float) -> float:
+    return lib().oracle_round_bf16(float(v))
+
+
+def plan(ids: np.ndarray, E: int) -> dict:
+    """Stable counting sort of the flat slots by expert id."""
+    T, K = ids.shape
+    N = T * K
+    ids64 = np.ascontiguousarray(ids, dtype=np.int64)
+    counts = np.zeros(E, np.int64)
+    offsets = np.zeros(E + 1, np.int64)
+    pos = np.zeros(N, np.int64)
+    src = np.zeros(N, np.int64)
+    bad = lib().oracle_plan(T, K, E, _p(ids64), _p(counts), _p(offsets), _p(pos), _p(src))
+    return dict(counts=counts, offsets=offsets, pos=pos, src=src, bad=int(bad))
+
+
+def full(x, ids, scores, w13, w2, dout=None, mode: str = "bf16") -> dict:
+    """Whole layer on small shapes: plan, forward, and backward when dout is given.
+
+    Returns every intermediate: xg, h13, a, y, out (+ dy, dscores, dh13, dxg, dx, dw13, dw2),
+    all float64, plus the plan arrays."""
+    T, D = x.shape
+    E, two, F, D2 = w13.shape
+    assert two == 2 and D2 == D and w2.shape == (E, D, F)
+    K = ids.shape[1]
+    N = T * K
+    idt = _in_dtype_of(x)
+    x, w13, w2 = (_as_input(a, idt) for a in (x, w13, w2))
+    dout = _as_input(dout, idt)
+    sh = _shape(T, D, F, E, K, mode, idt)
+    pl = plan(ids, E)
+    ids64 = np.ascontiguousarray(ids, dtype=np.int64)
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    res = dict(pl)
+    xg = np.zeros((N, D)); h13 = np.zeros((N, 2 * F)); a = np.zeros((N, F))
+    y = np.zeros((N, D)); out = np.zeros((T, D))
+    L = lib()
+    L.oracle_forward(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2), _p(pl["pos"]),
+                     _p(pl["src"]), _p(xg), _p(h13), _p(a), _p(y), _p(out))
+    res.update(xg=xg, h13=h13, a=a, y=y, out=out)
+    if dout is not None:
+        dy = np.zeros((N, D)); dscores = np.zeros((T, K)); dh13 = np.zeros((N, 2 * F))
+        dxg = np.zeros((N, D)); dx = np.zeros((T, D)); dw13 = np.zeros((E, 2, F, D))
+        dw2 = np.zeros((E, D, F))
+        L.oracle_backward(ctypes.byref(sh), _p(dout), _p(ids64), _p(sc), _p(w13), _p(w2),
+                          _p(pl["offsets"]), _p(pl["pos"]), _p(pl["src"]), _p(xg), _p(h13), _p(a),
+                          _p(y), _p(dy), _p(dscores), _p(dh13), _p(dxg), _p(dx), _p(dw13), _p(dw2))
+        res.update(dy=dy, dscores=dscores, dh13=dh13, dxg=dxg, dx=dx, dw13=dw13, dw2=dw2)
+    return res
+
+
+def tokens(x, ids, scores, w13, w2, toks, dout=None, mode: str = "bf16", want_y: bool = False):
+    """out (and dscores, dx when dout is given) for the listed tokens only, at any shape."""
+    T, D = x.shape
+    E, _, F, _ = w13.shape
+    K = ids.shape[1]
+    idt = _in_dtype_of(x)
+    x, w13, w2 = (_as_input(a, idt) for a in (x, w13, w2))
+    dout = _as_input(dout, idt)
+    sh = _shape(T, D, F, E, K, mode, idt)
+    toks = np.ascontiguousarray(toks, dtype=np.int64)
+    n = len(toks)
+    ids64 = np.ascontiguousarray(ids, dtype=np.int64)
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    out = np.zeros((n, D)); dsc = np.zeros((n, K)); dx = np.zeros((n, D))
+    yr = np.zeros((n, K, D)) if want_y else None
+    lib().oracle_tokens(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2), _p(dout), n,
+                        _p(toks), _p(out), _p(dsc), _p(dx), _p(yr))
+    res = dict(out=out)
+    if dout is not None:
+        res.update(dscores=dsc, dx=dx)
+    if want_y:
+        res["y"] = yr
+    return res
+
+
+def wgrad_entries(x, ids, scores, w13, w2, dout, e: int, jd: np.ndarray, df: np.ndarray,
+                  mode: str = "bf16"):
+    """dW13[e, j, d] for the (j, d) pairs in jd ([n,2], j in [0,2F)) and dW2[e, d, f] for the
+    (d, f) pairs in df ([m,2])."""
+    T, D = x.shape
+    E, _, F, _ = w13.shape
+    K = ids.shape[1]
+    idt = _in_dtype_of(x)
+    x, w13, w2, dout = (_as_input(a, idt) for a in (x, w13, w2, dout))
+    sh = _shape(T, D, F, E, K, mode, idt)
+    jd = np.ascontiguousarray(jd, dtype=np.int64).reshape(-1, 2)
+    df = np.ascontiguousarray(df, dtype=np.int64).reshape(-1, 2)
+    ids64 = np.ascontiguousarray(ids, dtype=np.int64)
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    v13 = np.zeros(len(jd)); v2 = np.zeros(len(df))
+    lib().oracle_wgrad_entries(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2),
+                               _p(dout), int(e), len(jd), _p(jd), _p(v13), len(df), _p(df), _p(v2))
+    return v13, v2
