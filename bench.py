@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-experts layer on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident in HBM:
+routing plan -> permute -> W13 grouped GEMM + SwiGLU -> W2 grouped GEMM -> combine, then the
+backward (combine transpose + dscores -> W2 DGRAD + SwiGLU derivative -> W2 WGRAD -> W13 DGRAD ->
+W13 WGRAD -> dX combine).
+
+    python bench.py [--steps K] [--warmup W] [--workload large_hidden] [--gpus 1]
+
+Prints one JSON line: whole-step bf16 TFLOP/s (algorithmic FLOPs 18*N*D*F per step, N = T*K
+routed rows) and tokens/s, the per-stage times from HIP events recorded on the layer's stream
+during the timed steps, the roofline fraction of the dominant kernel, and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+METRIC = "routed-expert fwd+bwd bf16 TFLOP/s and tokens/s on 1 MI355X; % MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(e)
+        return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(v), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return v.value
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+PLAN_STAGES = ["plan_hist", "plan_scan", "plan_scatter"]
+FWD_STAGES = ["permute", "fprop_w13_swiglu", "fprop_w2", "combine"]
+BWD_STAGES = ["combine_bwd_dscores", "dgrad_w2_swiglu", "wgrad_w2", "dgrad_w13", "wgrad_w13",
+              "dx_combine"]
+
+
+def stage_work(w):
+    """Algorithmic work per launch of each stage: ('mfma', FLOPs) or ('hbm', bytes)."""
+    N, T, D, F = w.N, w.T, w.D, w.F
+    return {
+        "permute": ("hbm", 2 * T * D + 2 * N * D),
+        "fprop_w13_swiglu": ("mfma", 4 * N * D * F),
+        "fprop_w2": ("mfma", 2 * N * D * F),
+        "combine": ("hbm", 2 * N * D + 2 * T * D),
+        "combine_bwd_dscores": ("hbm", 2 * T * D + 4 * N * D),
+        "dgrad_w2_swiglu": ("mfma", 2 * N * D * F),
+        "wgrad_w2": ("mfma", 2 * N * D * F),
+        "dgrad_w13": ("mfma", 4 * N * D * F),
+        "wgrad_w13": ("mfma", 4 * N * D * F),
+        "dx_combine": ("hbm", 2 * N * D + 2 * T * D),
+    }
+
+
+def cpu_baseline(inp, n_tokens):
+    import oracle
+    import workloads as W
+
+    w = inp.w
+    toks = W.sample_tokens(w.T, n_tokens, seed=1)
+    t0 = time.perf_counter()
+    oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks, inp.dout, mode="bf16")
+    dt = time.perf_counter() - t0
+    flops = 12 * w.K * w.D * w.F * len(toks)  # forward 6KDF + token-local backward 6KDF per token
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d seeded tokens of the %s workload: forward and the token-local backward "
+                  "(out, dscores, dx; weight gradients excluded), %.1f s, %.3g tokens/s"
+                  % (len(toks), w.name, dt, len(toks) / dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large_hidden")
+    ap.add_argument("--cpu-baseline-tokens", type=int, default=256,
+                    help="tokens in the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is one GPU's share of an "
+              "expert-parallel job and this build has no multi-GPU path (asked for --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from mixture_experts_routed_plan_amd import device as dv
+    from mixture_experts_routed_plan_amd import moe_trace
+
+    w = W.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = W.make_inputs(w, with_dout=True)
+    log("bench: %s inputs drawn in %.1fs" % (w.name, time.time() - t0))
+
+    torch.cuda.set_device(0)
+    x, w13, w2, dout = (dv.to_device_bits(a) for a in (inp.x, inp.w13, inp.w2, inp.dout))
+    ids = torch.from_numpy(inp.ids).cuda()
+    scores = torch.from_numpy(inp.scores).cuda()
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+
+    def make_trace(n):
+        tr = moe_trace()
+        tr.n_events = n
+        evs = [hip.create() for _ in range(n)]
+        for i, e in enumerate(evs):
+            tr.events[i] = e.value
+        return tr, evs
+
+    def step(traces=None):
+        tp, tf, tb = traces if traces else (None, None, None)
+        layer.plan(ids, stream, tp)
+        layer.forward(x, scores, w13, w2, stream, tf)
+        layer.backward(dout, scores, w13, w2, stream, tb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: %d warmup steps done" % args.warmup)
+
+    traces = [(make_trace(4), make_trace(5), make_trace(7)) for _ in range(args.steps)]
+    start, end = hip.create(), hip.create()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(start, stream)
+    for k in range(args.steps):
+        step(tuple(t[0] for t in traces[k]))
+    hip.record(end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hip.ms(start, end)
+    ms = total_ms / args.steps
+    log("bench: %d timed steps, %.3f ms/step (wall %.3f ms/step)" %
+        (args.steps, ms, 1e3 * wall / args.steps))
+
+    names = PLAN_STAGES + FWD_STAGES + BWD_STAGES
+    per = {n: [] for n in names}
+    for (tp, ep), (tf, ef), (tb, eb) in traces:
+        for lst, evs in ((PLAN_STAGES, ep), (FWD_STAGES, ef), (BWD_STAGES, eb)):
+            for i, n in enumerate(lst):
+                per[n].append(hip.ms(evs[i], evs[i + 1]))
+    work = stage_work(w)
+    stages = {}
+    for n in names:
+        avg = float(np.mean(per[n]))
+        ent = {"ms": round(avg, 4)}
+        if n in work:
+            kind, amount = work[n]
+            if kind == "mfma":
+                ent["tflops"] = round(amount / avg / 1e9, 1)
+                ent["frac_peak"] = round(amount / avg / 1e9 / PEAK_BF16_TFLOPS, 4)
+            else:
+                ent["gbs"] = round(amount / avg / 1e6, 1)
+                ent["frac_peak"] = round(amount / avg / 1e6 / PEAK_HBM_GBS, 4)
+        stages[n] = ent
+    dom = max(work, key=lambda n: stages[n]["ms"])
+    kind, amount = work[dom]
+    avg_s = stages[dom]["ms"] / 1e3
+    if kind == "mfma":
+        roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = amount
+
+    flops = 18 * w.N * w.D * w.F
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(w.T / (ms / 1e3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: T=%d D=%d F=%d E=%d K=%d, plan+forward+backward"
+                               % (w.name, w.T, w.D, w.F, w.E, w.K),
+                   "T": w.T, "D": w.D, "F": w.F, "E": w.E, "K": w.K,
+                   "routing": w.routing, "parallelism": "single GPU (one EP rank's share)"},
+        "roofline": roof,
+        "stages": stages,
+    }
+    hip.close()
+    if args.cpu_baseline_tokens > 0:
+        log("bench: timing the CPU oracle on %d tokens" % args.cpu_baseline_tokens)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_baseline_tokens)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * moe_routed.h -- C ABI of the MI355X (gfx950) routed-experts layer: one GPU's share of a
+ * mixture-of-experts layer, forward and backward.
+ *
+ * The operation (Dist-MoE 0.1.0 PyPI page, "Understand the execution model" and "BF16 Quickstart";
+ * TeraMoE README, worker list; MegaMoE ROCm Primus guide, introduction):
+ *
+ *   caller routing (x, top-k expert ids, top-k scores)
+ *     -> plan: group the T*K routed slots by expert (stable)
+ *     -> permute: copy each token row into its expert-grouped rows
+ *     -> W13 grouped GEMM (gate and up projections) with the SwiGLU activation
+ *     -> W2 grouped GEMM (down projection)
+ *     -> combine: score-weighted sum of each token's K expert rows, in token order
+ *   and the backward of all of it: dscores, DGRAD (input gradients) and WGRAD (weight gradients).
+ *
+ * Notation: T tokens, D hidden width, F per-expert intermediate width, E experts, K slots per
+ * token, N = T*K routed slots; slot i = t*K + k.
+ *
+ * Data types and layouts (all tensors dense, row-major, contiguous):
+ *   bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+ *   x[T,D] bf16 ............ token rows
+ *   topk_ids[T,K] .......... int32 or int64 (moe_shape.ids_dtype); expert of slot (t,k)
+ *   scores[T,K] fp32 ....... routing weight of slot (t,k)
+ *   w13[E,2,F,D] bf16 ...... w13[e,0] gate projection, w13[e,1] up projection, each [F,D]
+ *                            ([out,in]: g = w13[e,0] . x); the same bytes as [E,2F,D]
+ *   w2[E,D,F] bf16 ......... down projection [out,in]
+ *   out[T,D] bf16; dout[T,D] bf16; dx[T,D] bf16; dw13[E,2,F,D] bf16; dw2[E,D,F] bf16;
+ *   dscores[T,K] fp32.
+ *
+ * Numerics (Dist-MoE, "Choose a precision and pipeline", BF16): GEMM operands are bf16 and the
+ * products accumulate in fp32. Every stored intermediate (the gate/up pre-activations h13 = [g|u],
+ * the activation a = silu(g)*u, the expert outputs y, dy, dh13, dxg) and every output except
+ * dscores is rounded once to bf16 (nearest-even). The combine and the dX reduction add the K slots
+ * of a token in ascending k in fp32; no result depends on atomics or on scheduling, so repeated
+ * calls are bitwise identical.
+ *
+ * Ownership: the caller allocates every buffer (device memory) and owns it; the library holds no
+ * device state and allocates nothing. The plan, saved and workspace buffers are sized by the
+ * moe_*_bytes queries below, which are closed forms of the shape. x, scores, w13 and w2 must stay
+ * unchanged between moe_forward and the matching moe_backward; the plan and saved buffers carry
+ * state from moe_plan / moe_forward to later calls until the caller reuses them.
+ *
+ * Streams and synchronisation: every call only enqueues work on the given stream (0 = the null
+ * stream) and returns without waiting, except moe_plan_status, which waits for the stream. No
+ * launch size depends on the routing, so a fixed call sequence can be captured in a graph.
+ *
+ * Errors: a call returns MOE_OK or a negative moe_status. Host-side checks (null or misaligned
+ * pointers, bad shapes, unsupported dtypes) happen before anything is enqueued; on such an error
+ * nothing is enqueued and no buffer is touched. Expert ids outside [0,E) do not fault: that slot
+ * is dropped (no row; adds nothing to out, dx or the weight gradients; its dscore is 0) and
+ * counted in the plan's status word, which moe_plan_status reports as MOE_E_BAD_IDS.
+ * Duplicate ids within a token are legal: each slot is its own row.
+ */
+#ifndef MOE_ROUTED_H
+#define MOE_ROUTED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* moe_shape.ids_dtype */
+#define MOE_IDS_I32 0
+#define MOE_IDS_I64 1
+
+/* moe_shape.flags: keep the forward intermediates (xg, h13, a, y) in the saved buffer so that
+ * moe_backward can run. Without it the forward keeps its intermediates in the workspace and
+ * stores no h13. */
+#define MOE_SAVE_FOR_BACKWARD 1
+
+/* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64,
+ * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+
+typedef struct moe_shape {
+  int64_t T;         /* tokens */
+  int64_t D;         /* hidden width */
+  int64_t F;         /* per-expert intermediate width */
+  int64_t E;         /* experts on this GPU */
+  int64_t K;         /* routed slots per token */
+  int32_t ids_dtype; /* MOE_IDS_I32 or MOE_IDS_I64 */
+  int32_t flags;     /* 0 or MOE_SAVE_FOR_BACKWARD */
+} moe_shape;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_E_NULL = -1,    /* a required pointer is NULL */
+  MOE_E_SHAPE = -2,   /* shape outside the limits above */
+  MOE_E_ALIGN = -3,   /* a pointer is not 16-byte aligned (ids/scores: element aligned) */
+  MOE_E_DTYPE = -4,   /* ids_dtype or flags not recognised */
+  MOE_E_HIP = -5,     /* a HIP launch or runtime call failed */
+  MOE_E_BAD_IDS = -6, /* (moe_plan_status only) the routing held ids outside [0,E) */
+  MOE_E_STATE = -7    /* moe_backward on a shape without MOE_SAVE_FOR_BACKWARD */
+} moe_status;
+
+/* Optional stage timing: when a non-NULL moe_trace is passed, the call records
+ * events[0] on the stream before its first kernel and events[s+1] after stage s, for the first
+ * n_events events (the caller creates the events). Stages:
+ *   moe_plan:     0 block histograms, 1 scan + tile tables, 2 stable scatter
+ *   moe_forward:  0 permute, 1 W13 GEMM + SwiGLU, 2 W2 GEMM, 3 combine
+ *   moe_backward: 0 combine transpose + dscores, 1 DGRAD W2 + SwiGLU derivative, 2 WGRAD W2,
+ *                 3 DGRAD W13, 4 WGRAD W13, 5 dX combine                                         */
+#define MOE_TRACE_MAX_EVENTS 8
+typedef struct moe_trace {
+  int32_t n_events;
+  hipEvent_t events[MOE_TRACE_MAX_EVENTS];
+} moe_trace;
+
+/* Byte sizes of the caller-allocated buffers; 0 for a shape that fails the checks. */
+size_t moe_plan_bytes(const moe_shape* shape);
+size_t moe_saved_bytes(const moe_shape* shape);     /* 0 unless MOE_SAVE_FOR_BACKWARD */
+size_t moe_workspace_bytes(const moe_shape* shape); /* forward without save, and backward */
+
+/* Routing plan (Dist-MoE, "Understand the execution model": routing metadata is generated on the
+ * GPU from caller ids; TeraMoE README: the scheduler forms per-expert batches).
+ * From topk_ids[T,K] it builds, in plan (moe_plan_bytes, device):
+ *   counts[e] = #slots routed to e;  offsets[e] = sum of counts below e;
+ *   pos[i] = offsets[id_i] + #{j < i : id_j = id_i}  (stable expert-grouped row of slot i; -1 when
+ *            id_i is out of range);  src[pos[i]] = i;
+ *   the per-expert row-tile lists the grouped GEMMs walk, an expert order by decreasing count,
+ *   and the status word (number of out-of-range ids). */
+moe_status moe_plan(const moe_shape* shape, const void* topk_ids, void* plan, hipStream_t stream,
+                    const moe_trace* trace);
+
+/* Forward (Dist-MoE "Understand the execution model"; TeraMoE compute and combine workers;
+ * MegaMoE dispatch grouped GEMM -> SwiGLU -> grouped GEMM combine). With r = pos[t*K+k], e = id:
+ *   xg[r]   = x[t]                                           (permute)
+ *   g, u    = bf16(w13[e,0] . xg[r]), bf16(w13[e,1] . xg[r])  (gate/up grouped GEMM, fp32 acc)
+ *   a[r]    = bf16(silu(g) * u)                              (SwiGLU epilogue)
+ *   y[r]    = bf16(w2[e] . a[r])                             (down grouped GEMM)
+ *   out[t]  = bf16(sum_k scores[t,k] * y[pos[t*K+k]])        (combine, k ascending, fp32)
+ * plan: from moe_plan with the same shape and ids. saved (moe_saved_bytes) is required with
+ * MOE_SAVE_FOR_BACKWARD, workspace (moe_workspace_bytes) without it; the other may be NULL. */
+moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t* x,
+                       const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
+                       void* saved, void* workspace, hipStream_t stream, const moe_trace* trace);
+
+/* Backward of moe_forward (Dist-MoE: DGRAD and WGRAD; MegaMoE "Design": the down projection's
+ * weight gradient is produced before the gate/up one), given dout[T,D]:
+ *   dy[r]       = bf16(scores[t,k] * dout[t]);   dscores[t,k] = sum_d dout[t,d] * y[r,d]  (fp32)
+ *   da[r]       = w2[e]^T . dy[r]   (fp32, not stored);   with s = sigmoid(g):
+ *   dg          = bf16(da * u * s * (1 + g*(1 - s)));  du = bf16(da * g * s);  dh13[r] = [dg|du]
+ *   dw2[e]      = bf16(sum over e's rows of dy^T a)      (zero for an expert with no rows)
+ *   dxg[r]      = bf16(w13[e]^T . dh13[r])                (w13[e] viewed as [2F,D])
+ *   dw13[e]     = bf16(sum over e's rows of dh13^T xg)
+ *   dx[t]       = bf16(sum_k dxg[pos[t*K+k]])             (k ascending, fp32)
+ * dx, dw13 and dw2 are overwritten. Requires the shape's MOE_SAVE_FOR_BACKWARD and the saved
+ * buffer of the matching forward; workspace holds dy/dxg and dh13. */
+moe_status moe_backward(const moe_shape* shape, const void* plan, const void* saved,
+                        const uint16_t* dout, const float* scores, const uint16_t* w13,
+                        const uint16_t* w2, uint16_t* dx, uint16_t* dw13, uint16_t* dw2,
+                        float* dscores, void* workspace, hipStream_t stream,
+                        const moe_trace* trace);
+
+/* Copy the plan's integer arrays into caller device buffers (int32): counts[E], offsets[E+1],
+ * pos[N], src[N] (src entries past the last routed row are -1). Any of them may be NULL. */
+moe_status moe_plan_export(const moe_shape* shape, const void* plan, int32_t* counts,
+                           int32_t* offsets, int32_t* pos, int32_t* src, hipStream_t stream);
+
+/* Wait for the stream, then report the plan's status word: *bad_ids (host pointer, may be NULL)
+ * receives the number of out-of-range ids; returns MOE_E_BAD_IDS when it is non-zero. */
+moe_status moe_plan_status(const moe_shape* shape, const void* plan, int64_t* bad_ids,
+                           hipStream_t stream);
+
+/* Device pointers to the saved forward intermediates inside saved (for inspection and tests):
+ * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. */
+moe_status moe_saved_views(const moe_shape* shape, void* saved, uint16_t** xg, uint16_t** h13,
+                           uint16_t** a, uint16_t** y);
+
+const char* moe_status_str(int status);
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTED_H */

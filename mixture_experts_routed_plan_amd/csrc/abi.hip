@@ -1,0 +1,234 @@
+// C ABI of the routed-experts library: host-side checks, buffer layouts and the fixed launch
+// sequence of each call. No call allocates, and only moe_plan_status waits for the stream.
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_E_NULL;
+  if (s->ids_dtype != MOE_IDS_I32 && s->ids_dtype != MOE_IDS_I64) return MOE_E_DTYPE;
+  if (s->flags & ~MOE_SAVE_FOR_BACKWARD) return MOE_E_DTYPE;
+  if (s->T < 1 || s->K < 1 || s->K > MOE_MAX_TOPK) return MOE_E_SHAPE;
+  if (s->E < 1 || s->E > MOE_MAX_EXPERTS) return MOE_E_SHAPE;
+  if (s->D < 64 || s->F < 64 || (s->D % 64) != 0 || (s->F % 64) != 0) return MOE_E_SHAPE;
+  if (s->D > (1 << 24) || s->F > (1 << 24)) return MOE_E_SHAPE;
+  if (s->T > (int64_t)(INT32_MAX - 1) / s->K) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+struct Tracer {
+  const moe_trace* tr;
+  hipStream_t st;
+  int next;
+  hipError_t mark() {
+    if (!tr || next >= tr->n_events || next >= MOE_TRACE_MAX_EVENTS) return hipSuccess;
+    return hipEventRecord(tr->events[next++], st);
+  }
+};
+
+#define MOE_TRY(expr)                             \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return MOE_E_HIP;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "a required pointer is null";
+    case MOE_E_SHAPE: return "shape outside the supported limits";
+    case MOE_E_ALIGN: return "a pointer is not suitably aligned";
+    case MOE_E_DTYPE: return "ids dtype or flags not recognised";
+    case MOE_E_HIP: return "a HIP launch or runtime call failed";
+    case MOE_E_BAD_IDS: return "routing held expert ids outside [0, E)";
+    case MOE_E_STATE: return "backward needs a shape with MOE_SAVE_FOR_BACKWARD";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_plan_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return plan_layout(*s).total;
+}
+
+size_t moe_saved_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return 0;
+  return saved_layout(*s).total;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return work_layout(*s).total;
+}
+
+moe_status moe_plan(const moe_shape* s, const void* topk_ids, void* plan, hipStream_t stream,
+                    const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !plan) return MOE_E_NULL;
+  if (!aligned(topk_ids, s->ids_dtype == MOE_IDS_I64 ? 8 : 4) || !aligned(plan, 16))
+    return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, plan);
+  Tracer tr{trace, stream, 0};
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_hist(*s, L, p, topk_ids, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_scan(*s, L, p, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_scatter(*s, L, p, topk_ids, stream));
+  MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
+                       const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
+                       void* saved, void* workspace, hipStream_t stream, const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const bool save = (s->flags & MOE_SAVE_FOR_BACKWARD) != 0;
+  if (!plan || !x || !scores || !w13 || !w2 || !out) return MOE_E_NULL;
+  if (save ? !saved : !workspace) return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(out, 16) || !aligned(scores, 4) || (saved && !aligned(saved, 16)) ||
+      (workspace && !aligned(workspace, 16)))
+    return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, (void*)plan);
+  uint16_t *xg, *h13 = nullptr, *a, *y;
+  if (save) {
+    const SavedLayout S = saved_layout(*s);
+    char* b = (char*)saved;
+    xg = (uint16_t*)(b + S.xg);
+    h13 = (uint16_t*)(b + S.h13);
+    a = (uint16_t*)(b + S.a);
+    y = (uint16_t*)(b + S.y);
+  } else {
+    const WorkLayout W = work_layout(*s);
+    char* b = (char*)workspace;
+    xg = (uint16_t*)(b + W.xg);
+    a = (uint16_t*)(b + W.a);
+    y = (uint16_t*)(b + W.y);
+  }
+  Tracer tr{trace, stream, 0};
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_permute(*s, p.pos, x, xg, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_fprop_w13(*s, p, xg, w13, h13, a, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_fprop_w2(*s, p, a, w2, y, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_combine(*s, p.pos, y, scores, out, stream));
+  MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
+                        const uint16_t* dout, const float* scores, const uint16_t* w13,
+                        const uint16_t* w2, uint16_t* dx, uint16_t* dw13, uint16_t* dw2,
+                        float* dscores, void* workspace, hipStream_t stream,
+                        const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return MOE_E_STATE;
+  if (!plan || !saved || !dout || !scores || !w13 || !w2 || !dx || !dw13 || !dw2 || !dscores ||
+      !workspace)
+    return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(saved, 16) || !aligned(dout, 16) || !aligned(w13, 16) ||
+      !aligned(w2, 16) || !aligned(dx, 16) || !aligned(dw13, 16) || !aligned(dw2, 16) ||
+      !aligned(workspace, 16) || !aligned(scores, 4) || !aligned(dscores, 4))
+    return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, (void*)plan);
+  const SavedLayout S = saved_layout(*s);
+  const char* sb = (const char*)saved;
+  const uint16_t* xg = (const uint16_t*)(sb + S.xg);
+  const uint16_t* h13 = (const uint16_t*)(sb + S.h13);
+  const uint16_t* a = (const uint16_t*)(sb + S.a);
+  const uint16_t* y = (const uint16_t*)(sb + S.y);
+  const WorkLayout W = work_layout(*s);
+  char* wb = (char*)workspace;
+  uint16_t* dy = (uint16_t*)(wb + W.dy);
+  uint16_t* dh13 = (uint16_t*)(wb + W.dh13);
+  uint16_t* dxg = dy;  // dy is dead once the W2 weight gradient has been formed
+  Tracer tr{trace, stream, 0};
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_combine_bwd(*s, p.pos, dout, y, scores, dy, dscores, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_dgrad_w2(*s, p, dy, w2, h13, dh13, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_wgrad_w2(*s, p, dy, a, dw2, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_dgrad_w13(*s, p, dh13, w13, dxg, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_wgrad_w13(*s, p, dh13, xg, dw13, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_combine(*s, p.pos, dxg, nullptr, dx, stream));
+  MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
+moe_status moe_plan_export(const moe_shape* s, const void* plan, int32_t* counts,
+                           int32_t* offsets, int32_t* pos, int32_t* src, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!plan) return MOE_E_NULL;
+  if (!aligned(plan, 16)) return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, (void*)plan);
+  const size_t N = (size_t)L.N, E = (size_t)L.E;
+  if (counts)
+    MOE_TRY(hipMemcpyAsync(counts, p.counts, 4 * E, hipMemcpyDeviceToDevice, stream));
+  if (offsets)
+    MOE_TRY(hipMemcpyAsync(offsets, p.offsets, 4 * (E + 1), hipMemcpyDeviceToDevice, stream));
+  if (pos) MOE_TRY(hipMemcpyAsync(pos, p.pos, 4 * N, hipMemcpyDeviceToDevice, stream));
+  if (src) MOE_TRY(hipMemcpyAsync(src, p.src, 4 * N, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+moe_status moe_plan_status(const moe_shape* s, const void* plan, int64_t* bad_ids,
+                           hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!plan) return MOE_E_NULL;
+  if (!aligned(plan, 16)) return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, (void*)plan);
+  int32_t host = 0;
+  MOE_TRY(hipMemcpyAsync(&host, p.status, sizeof host, hipMemcpyDeviceToHost, stream));
+  MOE_TRY(hipStreamSynchronize(stream));
+  if (bad_ids) *bad_ids = host;
+  return host != 0 ? MOE_E_BAD_IDS : MOE_OK;
+}
+
+moe_status moe_saved_views(const moe_shape* s, void* saved, uint16_t** xg, uint16_t** h13,
+                           uint16_t** a, uint16_t** y) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return MOE_E_STATE;
+  if (!saved) return MOE_E_NULL;
+  const SavedLayout S = saved_layout(*s);
+  char* b = (char*)saved;
+  if (xg) *xg = (uint16_t*)(b + S.xg);
+  if (h13) *h13 = (uint16_t*)(b + S.h13);
+  if (a) *a = (uint16_t*)(b + S.a);
+  if (y) *y = (uint16_t*)(b + S.y);
+  return MOE_OK;
+}
+
+}  // extern "C"

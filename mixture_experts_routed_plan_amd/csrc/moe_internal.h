@@ -1,0 +1,179 @@
+// Internal declarations of the routed-experts library: buffer layouts (closed forms of the
+// shape), bf16 helpers for device code, and the kernel launchers the C ABI sequences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_routed.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------------
+// sizes and layouts
+
+constexpr int kPlanChunk = 1024;  // slots per plan workgroup (a multiple of 64)
+constexpr int kNumTileSizes = 3;  // row-tile lists kept in the plan: 64, 128, 256 rows
+constexpr int kTileRows[kNumTileSizes] = {64, 128, 256};
+constexpr int kStatusWords = 16;  // [0] out-of-range ids, [1 + s] row tiles for kTileRows[s]
+
+inline int tile_size_index(int bm) { return bm == 64 ? 0 : (bm == 128 ? 1 : 2); }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct PlanLayout {
+  int64_t N, E, NB;
+  size_t status, counts, offsets, pos, src, blkhist, blkbad, lpt, mtiles[kNumTileSizes], total;
+};
+
+inline PlanLayout plan_layout(const moe_shape& s) {
+  PlanLayout L{};
+  L.N = s.T * s.K;
+  L.E = s.E;
+  L.NB = ceil_div(L.N, kPlanChunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.status = take(sizeof(int32_t) * kStatusWords);
+  L.counts = take(sizeof(int32_t) * L.E);
+  L.offsets = take(sizeof(int32_t) * (L.E + 1));
+  L.pos = take(sizeof(int32_t) * L.N);
+  L.src = take(sizeof(int32_t) * L.N);
+  L.blkhist = take(sizeof(int32_t) * L.E * L.NB);
+  L.blkbad = take(sizeof(int32_t) * L.NB);
+  L.lpt = take(sizeof(int32_t) * L.E);
+  for (int t = 0; t < kNumTileSizes; ++t)
+    L.mtiles[t] = take(sizeof(int32_t) * 2 * (ceil_div(L.N, kTileRows[t]) + L.E));
+  L.total = o;
+  return L;
+}
+
+struct SavedLayout {
+  size_t xg, h13, a, y, total;
+};
+
+inline SavedLayout saved_layout(const moe_shape& s) {
+  SavedLayout L{};
+  const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.xg = take(2 * N * D);
+  L.h13 = take(2 * N * 2 * F);
+  L.a = take(2 * N * F);
+  L.y = take(2 * N * D);
+  L.total = o;
+  return L;
+}
+
+// Workspace: the forward without saving keeps xg, a, y here; the backward keeps dy (later reused
+// for dxg, once dy is dead) and dh13.
+struct WorkLayout {
+  size_t xg, a, y, fwd_total;
+  size_t dy, dh13, bwd_total;
+  size_t total;
+};
+
+inline WorkLayout work_layout(const moe_shape& s) {
+  WorkLayout L{};
+  const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
+  L.xg = 0;
+  L.a = align_up(2 * N * D, 256);
+  L.y = L.a + align_up(2 * N * F, 256);
+  L.fwd_total = L.y + align_up(2 * N * D, 256);
+  L.dy = 0;
+  L.dh13 = align_up(2 * N * D, 256);
+  L.bwd_total = L.dh13 + align_up(2 * N * 2 * F, 256);
+  L.total = L.fwd_total > L.bwd_total ? L.fwd_total : L.bwd_total;
+  return L;
+}
+
+// ------------------------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN -> canonical quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------------------------------
+// launchers (return hipSuccess or the launch error)
+
+struct PlanPtrs {
+  int32_t* status;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pos;
+  int32_t* src;
+  int32_t* blkhist;
+  int32_t* blkbad;
+  int32_t* lpt;
+  int32_t* mtiles[kNumTileSizes];
+};
+
+inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
+  char* b = (char*)base;
+  PlanPtrs p;
+  p.status = (int32_t*)(b + L.status);
+  p.counts = (int32_t*)(b + L.counts);
+  p.offsets = (int32_t*)(b + L.offsets);
+  p.pos = (int32_t*)(b + L.pos);
+  p.src = (int32_t*)(b + L.src);
+  p.blkhist = (int32_t*)(b + L.blkhist);
+  p.blkbad = (int32_t*)(b + L.blkbad);
+  p.lpt = (int32_t*)(b + L.lpt);
+  for (int t = 0; t < kNumTileSizes; ++t) p.mtiles[t] = (int32_t*)(b + L.mtiles[t]);
+  return p;
+}
+
+hipError_t launch_plan_hist(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                            const void* ids, hipStream_t st);
+hipError_t launch_plan_scan(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                            hipStream_t st);
+hipError_t launch_plan_scatter(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                               const void* ids, hipStream_t st);
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* pos, const uint16_t* x, uint16_t* xg,
+                          hipStream_t st);
+// out[t] = bf16(sum_k w_k * rows[pos[t*K+k]]) with w_k = scores[t*K+k], or 1 when scores == null
+hipError_t launch_combine(const moe_shape& s, const int32_t* pos, const uint16_t* rows,
+                          const float* scores, uint16_t* out, hipStream_t st);
+hipError_t launch_combine_bwd(const moe_shape& s, const int32_t* pos, const uint16_t* dout,
+                              const uint16_t* y, const float* scores, uint16_t* dy,
+                              float* dscores, hipStream_t st);
+
+// grouped GEMMs
+hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
+                            const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st);
+hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
+                           const uint16_t* w2, uint16_t* y, hipStream_t st);
+hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                           const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
+                           hipStream_t st);
+hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                           const uint16_t* a, uint16_t* dw2, hipStream_t st);
+hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
+                            const uint16_t* w13, uint16_t* dxg, hipStream_t st);
+hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
+                            const uint16_t* xg, uint16_t* dw13, hipStream_t st);
+
+}  // namespace moe

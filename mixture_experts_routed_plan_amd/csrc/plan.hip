@@ -1,0 +1,212 @@
+// Routing plan on the GPU: a stable counting sort of the T*K routed slots by expert id.
+//
+// Dist-MoE 0.1.0 (PyPI page), "Understand the execution model": the routing metadata is generated
+// on the GPU from the caller's expert ids. TeraMoE README, worker list: a scheduler forms
+// per-expert compute batches -- here the per-expert row-tile lists the grouped GEMMs walk.
+//
+// Three launches, all sized by the shape only (nothing is read back to the host):
+//   1. k_plan_hist    one wavefront per chunk of kPlanChunk slots: expert histogram in LDS.
+//   2. k_plan_scan    one workgroup: per-expert scan over chunks (chunk bases), counts, the
+//                     exclusive scan of counts (offsets), row-tile lists for 64/128/256-row
+//                     tiles, the expert order by decreasing count, the out-of-range total.
+//   3. k_plan_scatter one wavefront per chunk, slots in ascending order, 64 at a time: lanes that
+//                     share an expert id find each other with one ballot per id bit, take
+//                     consecutive rows after the expert's running base in lane order, and the
+//                     lowest such lane advances the base. This keeps the order of equal ids
+//                     (stable), so pos/src are unique and match a sequential counting sort.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename IdT>
+__device__ __forceinline__ int load_expert(const IdT* ids, int i, int E) {
+  const IdT v = ids[i];
+  return (v >= 0 && v < (IdT)E) ? (int)v : -1;
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(64) void k_plan_hist(const IdT* __restrict__ ids, int N, int E,
+                                                  int NB, int32_t* __restrict__ blkhist,
+                                                  int32_t* __restrict__ blkbad) {
+  __shared__ int32_t h[MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x, b = blockIdx.x;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  const int lo = b * kPlanChunk, hi = min(N, lo + kPlanChunk);
+  int bad = 0;
+  for (int i = lo + lane; i < hi; i += 64) {
+    const int v = load_expert(ids, i, E);
+    if (v >= 0)
+      atomicAdd(&h[v], 1);
+    else
+      ++bad;
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) blkhist[(int64_t)e * NB + b] = h[e];
+  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+  if (lane == 0) blkbad[b] = bad;
+}
+
+// inclusive scan over the 1024 threads of the workgroup (scratch: 16 ints of LDS)
+__device__ __forceinline__ int block_scan_1024(int v, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? wsum[lane] : 0;
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(w, off);
+      if (lane >= off) w += o;
+    }
+    if (lane < 16) wsum[lane] = w;
+  }
+  __syncthreads();
+  const int add = wave > 0 ? wsum[wave - 1] : 0;
+  __syncthreads();  // wsum may be reused by the next call
+  return v + add;
+}
+
+__global__ __launch_bounds__(1024) void k_plan_scan(int N, int E, int NB, int32_t* status,
+                                                    int32_t* counts, int32_t* offsets,
+                                                    int32_t* blkhist, const int32_t* blkbad,
+                                                    int32_t* lpt, int32_t* src, int32_t* mt64,
+                                                    int32_t* mt128, int32_t* mt256) {
+  __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x;
+
+  // chunk bases within each expert (exclusive scan over chunks, in place) and the counts
+  int cnt = 0;
+  if (tid < E) {
+    int32_t* row = blkhist + (int64_t)tid * NB;
+    for (int b = 0; b < NB; ++b) {
+      const int v = row[b];
+      row[b] = cnt;
+      cnt += v;
+    }
+    counts[tid] = cnt;
+  }
+  s_cnt[tid] = cnt;
+  const int incl = block_scan_1024(cnt, wsum);
+  s_off[tid] = incl - cnt;
+  if (tid == 1023) s_off[MOE_MAX_EXPERTS] = incl;
+  __syncthreads();
+  const int nvalid = s_off[MOE_MAX_EXPERTS];
+  if (tid < E) offsets[tid] = s_off[tid];
+  if (tid == 0) offsets[E] = nvalid;
+
+  // row-tile lists: (expert, first row) of every tile of tile_rows rows, experts ascending
+  int32_t* lists[kNumTileSizes] = {mt64, mt128, mt256};
+  for (int t = 0; t < kNumTileSizes; ++t) {
+    const int bm = kTileRows[t];
+    const int nt = tid < E ? (cnt + bm - 1) / bm : 0;
+    const int ti = block_scan_1024(nt, wsum);
+    if (tid < E) {
+      int2* list = (int2*)lists[t];
+      const int start = ti - nt;
+      for (int q = 0; q < nt; ++q) list[start + q] = make_int2(tid, s_off[tid] + q * bm);
+    }
+    if (tid == 1023) status[1 + t] = ti;
+  }
+
+  // experts by decreasing count (ties: lower index first)
+  if (tid < E) {
+    int rank = 0;
+    for (int e2 = 0; e2 < E; ++e2) {
+      const int c2 = s_cnt[e2];
+      rank += (c2 > cnt) || (c2 == cnt && e2 < tid);
+    }
+    lpt[rank] = tid;
+  }
+
+  // rows past the last routed row have no source slot
+  for (int r = nvalid + tid; r < N; r += 1024) src[r] = -1;
+
+  if (tid == 0) {
+    int bad = 0;
+    for (int b = 0; b < NB; ++b) bad += blkbad[b];
+    status[0] = bad;
+    for (int w = 1 + kNumTileSizes; w < kStatusWords; ++w) status[w] = 0;
+  }
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(64) void k_plan_scatter(const IdT* __restrict__ ids, int N, int E,
+                                                     int NB, int nbits,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ blkhist,
+                                                     int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ src) {
+  __shared__ int32_t base[MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x, b = blockIdx.x;
+  for (int e = lane; e < E; e += 64) base[e] = offsets[e] + blkhist[(int64_t)e * NB + b];
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int lo = b * kPlanChunk, hi = min(N, lo + kPlanChunk);
+  for (int i0 = lo; i0 < hi; i0 += 64) {
+    const int i = i0 + lane;
+    const bool in = i < hi;
+    const int v = in ? load_expert(ids, i, E) : -1;
+    const bool ok = v >= 0;
+    // lanes holding the same expert id: agree on every bit of the id
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool one = ((v >> bit) & 1) != 0;
+      const uint64_t m = __ballot(ok && one);
+      peers &= one ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    const int cnt = __popcll(peers);
+    int p = -1;
+    if (ok) p = base[v] + rank;
+    __syncthreads();
+    if (in) pos[i] = p;
+    if (ok) src[p] = i;
+    if (ok && rank == 0) base[v] += cnt;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan_hist(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                            const void* ids, hipStream_t st) {
+  const int N = (int)L.N, E = (int)s.E, NB = (int)L.NB;
+  if (s.ids_dtype == MOE_IDS_I64)
+    hipLaunchKernelGGL(k_plan_hist<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids, N,
+                       E, NB, p.blkhist, p.blkbad);
+  else
+    hipLaunchKernelGGL(k_plan_hist<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids, N,
+                       E, NB, p.blkhist, p.blkbad);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_scan(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, (int)L.N, (int)s.E, (int)L.NB,
+                     p.status, p.counts, p.offsets, p.blkhist, p.blkbad, p.lpt, p.src,
+                     p.mtiles[0], p.mtiles[1], p.mtiles[2]);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_scatter(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
+                               const void* ids, hipStream_t st) {
+  const int N = (int)L.N, E = (int)s.E, NB = (int)L.NB;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (s.ids_dtype == MOE_IDS_I64)
+    hipLaunchKernelGGL(k_plan_scatter<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids,
+                       N, E, NB, nbits, p.offsets, p.blkhist, p.pos, p.src);
+  else
+    hipLaunchKernelGGL(k_plan_scatter<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids,
+                       N, E, NB, nbits, p.offsets, p.blkhist, p.pos, p.src);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,177 @@
+// Row kernels between token order and expert-grouped order (HBM-bound copies and reductions).
+//
+//   permute      xg[pos[t,k]] = x[t]   -- TeraMoE README, dispatch worker (writes the expert
+//                inputs); MoonEP FAQ (tokens written straight into expert-grouped positions).
+//                Token-major: each token row is read once and written K times.
+//   combine      out[t] = bf16(sum_k w_k * y[pos[t,k]]), k ascending, fp32, no atomics --
+//                TeraMoE combine worker (weighted accumulation) and gather worker (several
+//                results of one token reduced locally). With unit weights it is the dX reduction.
+//   combine_bwd  dy[pos[t,k]] = bf16(s[t,k] * dout[t]) and dscores[t,k] = <dout[t], y[pos[t,k]]>
+//                -- the transpose of combine and the derivative with respect to the scores.
+//
+// One wavefront per token; every lane moves 16-byte chunks (8 bf16), so one wavefront instruction
+// touches 1 KiB of a row. The K slots of a token are wave-uniform (pos and scores come through
+// scalar loads), so a dropped slot (pos < 0) is a uniform branch.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRowWaves = 4;  // tokens per 256-thread workgroup
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = bf16_to_f32(v.x & 0xffffu); f[1] = bf16_to_f32(v.x >> 16);
+  f[2] = bf16_to_f32(v.y & 0xffffu); f[3] = bf16_to_f32(v.y >> 16);
+  f[4] = bf16_to_f32(v.z & 0xffffu); f[5] = bf16_to_f32(v.z >> 16);
+  f[6] = bf16_to_f32(v.w & 0xffffu); f[7] = bf16_to_f32(v.w >> 16);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
+                                                 const int32_t* __restrict__ pos,
+                                                 uint4* __restrict__ xg, int T, int K, int nch) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint4* xr = x + (int64_t)t * nch;
+  const int32_t* pt = pos + (int64_t)t * K;
+  int c = lane;
+  for (; c + 192 < nch; c += 256) {
+    const uint4 v0 = xr[c], v1 = xr[c + 64], v2 = xr[c + 128], v3 = xr[c + 192];
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if (p < 0) continue;
+      uint4* dst = xg + (int64_t)p * nch + c;
+      dst[0] = v0; dst[64] = v1; dst[128] = v2; dst[192] = v3;
+    }
+  }
+  for (; c < nch; c += 64) {
+    const uint4 v = xr[c];
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if (p >= 0) xg[(int64_t)p * nch + c] = v;
+    }
+  }
+}
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ rows,
+                                                 const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ scores,
+                                                 uint4* __restrict__ out, int T, int K, int nch) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* pt = pos + (int64_t)t * K;
+  const float* st = WEIGHTED ? scores + (int64_t)t * K : nullptr;
+  int c = lane;
+  for (; c + 64 < nch; c += 128) {
+    float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, a1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if (p < 0) continue;
+      const float w = WEIGHTED ? st[k] : 1.0f;
+      const uint4* r = rows + (int64_t)p * nch + c;
+      const uint4 v0 = r[0], v1 = r[64];
+      float f0[8], f1[8];
+      unpack8(v0, f0);
+      unpack8(v1, f1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        a0[q] += w * f0[q];
+        a1[q] += w * f1[q];
+      }
+    }
+    out[(int64_t)t * nch + c] = pack8(a0);
+    out[(int64_t)t * nch + c + 64] = pack8(a1);
+  }
+  for (; c < nch; c += 64) {
+    float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if (p < 0) continue;
+      const float w = WEIGHTED ? st[k] : 1.0f;
+      float f0[8];
+      unpack8(rows[(int64_t)p * nch + c], f0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a0[q] += w * f0[q];
+    }
+    out[(int64_t)t * nch + c] = pack8(a0);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_combine_bwd(const uint4* __restrict__ dout,
+                                                     const uint4* __restrict__ y,
+                                                     const int32_t* __restrict__ pos,
+                                                     const float* __restrict__ scores,
+                                                     uint4* __restrict__ dy,
+                                                     float* __restrict__ dscores, int T, int K,
+                                                     int nch) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint4* dr = dout + (int64_t)t * nch;
+  for (int k = 0; k < K; ++k) {
+    const int p = pos[(int64_t)t * K + k];
+    if (p < 0) {
+      if (lane == 0) dscores[(int64_t)t * K + k] = 0.0f;
+      continue;
+    }
+    const float s = scores[(int64_t)t * K + k];
+    const uint4* yr = y + (int64_t)p * nch;
+    uint4* dyr = dy + (int64_t)p * nch;
+    float part = 0.0f;
+    for (int c = lane; c < nch; c += 64) {
+      float fd[8], fy[8], o[8];
+      unpack8(dr[c], fd);
+      unpack8(yr[c], fy);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        part += fd[q] * fy[q];
+        o[q] = s * fd[q];
+      }
+      dyr[c] = pack8(o);
+    }
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) dscores[(int64_t)t * K + k] = part;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* pos, const uint16_t* x, uint16_t* xg,
+                          hipStream_t st) {
+  const int T = (int)s.T;
+  hipLaunchKernelGGL(k_permute, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
+                     (const uint4*)x, pos, (uint4*)xg, T, (int)s.K, (int)(s.D / 8));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_shape& s, const int32_t* pos, const uint16_t* rows,
+                          const float* scores, uint16_t* out, hipStream_t st) {
+  const int T = (int)s.T;
+  const dim3 grid((T + kRowWaves - 1) / kRowWaves);
+  if (scores)
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
+                       (uint4*)out, T, (int)s.K, (int)(s.D / 8));
+  else
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
+                       (uint4*)out, T, (int)s.K, (int)(s.D / 8));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const moe_shape& s, const int32_t* pos, const uint16_t* dout,
+                              const uint16_t* y, const float* scores, uint16_t* dy,
+                              float* dscores, hipStream_t st) {
+  const int T = (int)s.T;
+  hipLaunchKernelGGL(k_combine_bwd, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
+                     (const uint4*)dout, (const uint4*)y, pos, scores, (uint4*)dy, dscores, T,
+                     (int)s.K, (int)(s.D / 8));
+  return hipGetLastError();
+}
+
+}  // namespace moe

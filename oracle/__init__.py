@@ -37,11 +37,11 @@ class _Shape(ctypes.Structure):
 
 
 def build(force: bool = True) -> str:
-    """Compile moe_oracle.c into liboracle.so (gcc -O2 -fopenmp, no fast-math)."""
+    """Compile moe_oracle.c into liboracle.so (gcc -O2 -fopenmp; no fast-math, no FMA contraction)."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-Wno-unused-parameter", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
@@ -58,6 +58,8 @@ def lib():
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
             S = ctypes.POINTER(_Shape)
+            L.oracle_num_threads.restype = ctypes.c_int
+            L.oracle_num_threads.argtypes = []
             L.oracle_round_bf16.restype = ctypes.c_double
             L.oracle_round_bf16.argtypes = [ctypes.c_double]
             L.oracle_plan.restype = I64
@@ -96,6 +98,10 @@ def _as_input(a, in_dtype):
 
 def _in_dtype_of(x):
     return IN_BF16 if x.dtype == np.uint16 else IN_F64
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
 
 
 def round_bf16(v: float) -> float:

@@ -36,6 +36,7 @@
  * an array of doubles (bf16-representable values when round_bf16 = 1).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -85,6 +86,9 @@ static inline double R(const oracle_shape* s, double v) {
 }
 
 static inline double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* threads the OpenMP loops below use */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------------------- */
 /* routing plan: a stable counting sort of the flat slots i = t*K + k by expert id               */
@@ -168,13 +172,33 @@ static void swiglu_grad(const oracle_shape* s, double da, double g, double u, do
   *du = R(s, da * g * sg);
 }
 
-/* dxg[d] = R(sum_j W13[e][j][d] * dh[j]) over j in [0, 2F) */
-static double dxg_elem(const oracle_shape* s, const void* w13, int64_t e, int64_t d,
-                       const double* dh) {
+/* dxg[d] = R(sum_j W13[e][j][d] * dh[j]) over j in [0, 2F), for every d. The loop runs over j
+ * outside and d inside so that W13[e] is read along its rows; every dxg[d] still adds its terms in
+ * ascending j. */
+static void dxg_row(const oracle_shape* s, const void* w13, int64_t e, const double* dh,
+                    double* dxg) {
   const int64_t D = s->D, F = s->F;
-  double acc = 0.0;
-  for (int64_t j = 0; j < 2 * F; ++j) acc += ld(w13, (e * 2 * F + j) * D + d, s->in_dtype) * dh[j];
-  return R(s, acc);
+  for (int64_t d = 0; d < D; ++d) dxg[d] = 0.0;
+  for (int64_t j = 0; j < 2 * F; ++j) {
+    const double v = dh[j];
+    const int64_t base = (e * 2 * F + j) * D;
+    for (int64_t d = 0; d < D; ++d) dxg[d] += ld(w13, base + d, s->in_dtype) * v;
+  }
+  for (int64_t d = 0; d < D; ++d) dxg[d] = R(s, dxg[d]);
+}
+
+/* da[f] = sum_d W2[e][d][f] * dyrow[d] for every f (transient, not rounded). Loop order as in
+ * dxg_row: d outside, f inside; every da[f] adds its terms in ascending d, the same sum as
+ * da_elem. */
+static void da_row(const oracle_shape* s, const void* w2, int64_t e, const double* dyrow,
+                   double* da) {
+  const int64_t D = s->D, F = s->F;
+  for (int64_t f = 0; f < F; ++f) da[f] = 0.0;
+  for (int64_t d = 0; d < D; ++d) {
+    const double v = dyrow[d];
+    const int64_t base = (e * D + d) * F;
+    for (int64_t f = 0; f < F; ++f) da[f] += ld(w2, base + f, s->in_dtype) * v;
+  }
 }
 
 /* Forward of one routed row: h[2F], a[F], y[D] from xrow[D] through expert e. */
@@ -192,12 +216,12 @@ static void row_backward(const oracle_shape* s, const void* w13, const void* w2,
                          double score, const double* doutrow, const double* h, double* dy,
                          double* dh, double* dxg) {
   const int64_t D = s->D, F = s->F;
+  double* da = (double*)malloc(sizeof(double) * F);
   for (int64_t d = 0; d < D; ++d) dy[d] = R(s, score * doutrow[d]);
-  for (int64_t f = 0; f < F; ++f) {
-    const double da = da_elem(s, w2, e, f, dy);
-    swiglu_grad(s, da, h[f], h[F + f], &dh[f], &dh[F + f]);
-  }
-  for (int64_t d = 0; d < D; ++d) dxg[d] = dxg_elem(s, w13, e, d, dh);
+  da_row(s, w2, e, dy, da);
+  for (int64_t f = 0; f < F; ++f) swiglu_grad(s, da[f], h[f], h[F + f], &dh[f], &dh[F + f]);
+  dxg_row(s, w13, e, dh, dxg);
+  free(da);
 }
 
 static void load_row(const oracle_shape* s, const void* p, int64_t row, double* dst) {

@@ -1,0 +1,118 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every entry point the header
+declares, and its host-side checks reject bad arguments before anything is enqueued (the failing
+calls below never reach a HIP call, so they are safe without a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_routed.h")
+LIB = os.path.join(ROOT, "mixture_experts_routed_plan_amd", "libmoe_routed.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from mixture_experts_routed_plan_amd import build as b
+        b.build()
+
+
+_ensure_built()
+import mixture_experts_routed_plan_amd as M  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"moe_plan", "moe_forward", "moe_backward"} <= set(names)
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", nm))
+    assert set(names) <= exported
+    assert set(M.EXPORTED) == set(names)
+
+
+def test_abi_version_and_status_strings():
+    assert M.moe_abi_version() == 1
+    for st in range(0, -8, -1):
+        assert M.moe_status_str(st) != "unknown status"
+    assert M.moe_status_str(-99) == "unknown status"
+
+
+def shape(**kw):
+    d = dict(T=64, D=256, F=128, E=8, K=2, ids_dtype=M.MOE_IDS_I64, save_for_backward=True)
+    d.update(kw)
+    return M.make_shape(**d)
+
+
+def test_sizes_are_closed_forms_of_the_shape():
+    s = shape()
+    N = 64 * 2
+    assert M.moe_plan_bytes(s) >= 4 * (8 + 9 + 2 * N)
+    assert M.moe_saved_bytes(s) >= 2 * N * (256 + 2 * 128 + 128 + 256)
+    assert M.moe_workspace_bytes(s) >= 2 * N * (256 + 2 * 128)
+    assert M.moe_saved_bytes(shape(save_for_backward=False)) == 0
+    big = shape(T=640)
+    assert M.moe_plan_bytes(big) > M.moe_plan_bytes(s)
+    assert M.moe_saved_bytes(big) > M.moe_saved_bytes(s)
+
+
+@pytest.mark.parametrize("kw", [dict(T=0), dict(K=0), dict(K=65), dict(E=0), dict(E=1025),
+                                dict(D=100), dict(F=96), dict(D=32), dict(T=2 ** 30, K=4)])
+def test_bad_shapes_rejected(kw):
+    s = shape(**kw)
+    assert M.moe_plan_bytes(s) == 0
+    assert M.moe_workspace_bytes(s) == 0
+    assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_SHAPE
+
+
+def test_bad_dtype_and_flags_rejected():
+    s = shape()
+    s.ids_dtype = 7
+    assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_DTYPE
+    s = shape()
+    s.flags = 6
+    assert M.moe_plan_bytes(s) == 0
+    assert M.moe_forward(s, 256, 256, 256, 256, 256, 256, 256, 256, 0) == M.MOE_E_DTYPE
+
+
+def test_null_and_alignment_rejected():
+    s = shape()
+    assert M.moe_plan(s, None, 256, 0) == M.MOE_E_NULL
+    assert M.moe_plan(s, 256, None, 0) == M.MOE_E_NULL
+    assert M.moe_plan(s, 260, 256, 0) == M.MOE_E_ALIGN  # int64 ids need 8-byte alignment
+    assert M.moe_plan(s, 256, 264, 0) == M.MOE_E_ALIGN  # plan needs 16 bytes
+    a = 4096
+    assert M.moe_forward(s, a, a, a, a, a, None, a, a, 0) == M.MOE_E_NULL
+    assert M.moe_forward(s, a, a + 8, a, a, a, a, a, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_forward(s, a, a, a + 2, a, a, a, a, a, 0) == M.MOE_E_ALIGN
+    # forward with saving needs the saved buffer; without saving it needs the workspace
+    assert M.moe_forward(s, a, a, a, a, a, a, None, a, 0) == M.MOE_E_NULL
+    s2 = shape(save_for_backward=False)
+    assert M.moe_forward(s2, a, a, a, a, a, a, a, None, 0) == M.MOE_E_NULL
+    args = [a] * 11
+    assert M.moe_backward(s, *args[:3], None, *args[4:11], stream=0) == M.MOE_E_NULL
+    assert M.moe_backward(s2, *args, stream=0) == M.MOE_E_STATE
+    assert M.moe_backward(s, a, a, a, a, a, a, a + 4, a, a, a, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_plan_export(s, None, stream=0) == M.MOE_E_NULL
+    assert M.moe_plan_status(s, None, 0)[0] == M.MOE_E_NULL
+
+
+def test_importing_without_the_library_fails_loudly(tmp_path):
+    code = ("import sys, os; sys.path.insert(0, %r); import mixture_experts_routed_plan_amd as M"
+            % str(tmp_path))
+    pkg = tmp_path / "mixture_experts_routed_plan_amd"
+    pkg.mkdir()
+    src = open(os.path.join(ROOT, "mixture_experts_routed_plan_amd", "__init__.py")).read()
+    (pkg / "__init__.py").write_text(src)
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+* plan (counts, offsets, pos, src): bit-exact, every workload, int32 and int64 ids;
+* permute (xg): bit-exact (a copy);
+* every floating output, widened to double: max|gpu - oracle| <= 2e-2 * max(1, max|oracle|) per
+  tensor (see assert_close); the oracle evaluates the same bf16 storage points with exact
+  (double) sums, so the bound covers fp32 accumulation order and the one-ulp flips of stored bf16
+  intermediates that it causes;
+* small shapes (several 256-row tiles per expert, ragged tails, an intermediate width that is not
+  a multiple of 128, skewed and duplicate routing, an empty expert): every element;
+* the five full-size workloads, in the launch configuration the benchmark times: the plan and xg
+  in full, out/dx/dscores on a seeded sample of 256 tokens, and sampled entries of the weight
+  gradients of 4 experts (most loaded, least loaded, two seeded others).
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-2
+
+
+def _lib():
+    import mixture_experts_routed_plan_amd as M
+    from mixture_experts_routed_plan_amd import device as dv
+    return M, dv
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def assert_close(name, got, ref, rtol=RTOL):
+    """The stated tolerance, per tensor: max|gpu - ref| <= rtol * max(1, max|ref|).
+
+    It is a normwise bound: the GPU accumulates in fp32 in MFMA order while the oracle sums
+    exactly, so about 1e-4..1e-2 of the stored bf16 intermediates (more for longer sums) land one
+    ulp apart, and every later sum that consumes them carries those ulps along; for a long
+    reduction (dscores over D terms) the carried ulps random-walk to a fixed absolute size that
+    an elementwise bound on a near-zero result cannot hold. The elementwise statistics and the
+    fraction of bitwise-equal elements are logged."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), name
+    if got.size == 0:
+        return
+    diff = np.abs(got - ref)
+    norm = float(diff.max()) / max(1.0, float(np.abs(ref).max()))
+    elem = diff / np.maximum(1.0, np.abs(ref))
+    log("  %-8s normwise %.3e  elementwise max %.3e (%d over %.0e)  exact %.4f  n %d"
+        % (name, norm, float(elem.max()), int((elem > rtol).sum()), rtol,
+           float((got == ref).mean()), got.size))
+    assert norm <= rtol, "%s: normwise error %.3e exceeds %.0e (worst at %s)" % (
+        name, norm, rtol, np.unravel_index(np.argmax(diff), diff.shape))
+
+
+def upload(inp, ids_dtype=np.int64):
+    _, dv = _lib()
+    d = dict(x=dv.to_device_bits(inp.x), w13=dv.to_device_bits(inp.w13),
+             w2=dv.to_device_bits(inp.w2),
+             ids=torch.from_numpy(np.ascontiguousarray(inp.ids.astype(ids_dtype))).cuda(),
+             scores=torch.from_numpy(inp.scores).cuda())
+    if inp.dout is not None:
+        d["dout"] = dv.to_device_bits(inp.dout)
+    return d
+
+
+def run(inp, ids_dtype=np.int64, backward=True, save=True):
+    _, dv = _lib()
+    w = inp.w
+    d = upload(inp, ids_dtype)
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, ids_dtype=ids_dtype, save_for_backward=save)
+    layer.plan(d["ids"])
+    layer.forward(d["x"], d["scores"], d["w13"], d["w2"])
+    if backward:
+        layer.backward(d["dout"], d["scores"], d["w13"], d["w2"])
+    torch.cuda.synchronize()
+    return layer, d
+
+
+def plan_check(layer, ids, E):
+    got = layer.plan_arrays()
+    ref = oracle.plan(ids, E)
+    for k in ("counts", "offsets", "pos", "src"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    st, bad = layer.plan_status()
+    assert bad == ref["bad"]
+    return got
+
+
+# ------------------------------------------------------------------------------------------------
+# plan
+
+PLAN_CASES = list(W.WORKLOADS) + list(W.PARITY_WORKLOADS)
+
+
+@pytest.mark.parametrize("ids_dtype", [np.int64, np.int32])
+@pytest.mark.parametrize("name", PLAN_CASES)
+def test_plan_bit_exact(name, ids_dtype):
+    M, dv = _lib()
+    w = {**W.WORKLOADS, **W.PARITY_WORKLOADS}[name]
+    ids, _ = W.routing(w, ids_dtype)
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, ids_dtype=ids_dtype, save_for_backward=False,
+                     alloc_grads=False)
+    layer.plan(torch.from_numpy(ids).cuda())
+    plan_check(layer, ids, w.E)
+    assert layer.plan_status() == (M.MOE_OK, 0)
+
+
+@pytest.mark.parametrize("ids_dtype", [np.int64, np.int32])
+def test_plan_out_of_range_and_duplicate_ids(ids_dtype):
+    M, dv = _lib()
+    rng = np.random.default_rng(5)
+    T, K, E = 3000, 4, 37
+    ids = rng.integers(0, E, (T, K))  # duplicates within a token
+    bad_at = rng.choice(T * K, 50, replace=False)
+    ids.ravel()[bad_at] = rng.choice([-1, -7, E, E + 100, 2 ** 31 - 1], 50)
+    ids = ids.astype(ids_dtype)
+    layer = dv.Layer(T, 64, 64, E, K, ids_dtype=ids_dtype, save_for_backward=False,
+                     alloc_grads=False)
+    layer.plan(torch.from_numpy(ids).cuda())
+    plan_check(layer, ids, E)
+    st, bad = layer.plan_status()
+    assert st == M.MOE_E_BAD_IDS and bad == 50
+
+
+def test_plan_many_experts_single_token_chunks():
+    _, dv = _lib()
+    rng = np.random.default_rng(6)
+    for T, K, E in ((1, 1, 1), (1, 64, 1024), (5, 3, 1000), (2049, 1, 1024), (777, 13, 2)):
+        ids = rng.integers(0, E, (T, K)).astype(np.int64)
+        layer = dv.Layer(T, 64, 64, E, K, save_for_backward=False, alloc_grads=False)
+        layer.plan(torch.from_numpy(ids).cuda())
+        plan_check(layer, ids, E)
+
+
+# ------------------------------------------------------------------------------------------------
+# whole layer, every element
+
+FULL_CASES = ["tiny", "p_ragged", "p_skew", "p_wide"]
+
+
+def _full_check(inp, layer):
+    _, dv = _lib()
+    w = inp.w
+    ref = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16")
+    pl = plan_check(layer, inp.ids, w.E)
+    sv = layer.saved_arrays()
+    nv = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(sv["xg"][:nv], inp.x[pl["src"][:nv] // w.K])
+    assert_close("h13", dv.bits_to_f64(sv["h13"][:nv]), ref["h13"][:nv])
+    assert_close("a", dv.bits_to_f64(sv["a"][:nv]), ref["a"][:nv])
+    assert_close("y", dv.bits_to_f64(sv["y"][:nv]), ref["y"][:nv])
+    assert_close("out", dv.bits_to_f64(dv.to_host_bits(layer.out)), ref["out"])
+    assert_close("dscores", layer.dscores.cpu().numpy(), ref["dscores"])
+    assert_close("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx)), ref["dx"])
+    assert_close("dw2", dv.bits_to_f64(dv.to_host_bits(layer.dw2)), ref["dw2"])
+    assert_close("dw13", dv.bits_to_f64(dv.to_host_bits(layer.dw13)), ref["dw13"])
+    return ref
+
+
+@pytest.mark.parametrize("name", FULL_CASES)
+def test_layer_parity_every_element(name):
+    w = {**W.WORKLOADS, **W.PARITY_WORKLOADS}[name]
+    inp = W.make_inputs(w)
+    log("\n[%s] T=%d D=%d F=%d E=%d K=%d" % (name, w.T, w.D, w.F, w.E, w.K))
+    layer, _ = run(inp)
+    _full_check(inp, layer)
+
+
+def test_layer_parity_int32_ids_and_bad_ids():
+    w = W.PARITY_WORKLOADS["p_ragged"].with_(T=333)
+    inp = W.make_inputs(w, ids_dtype=np.int32)
+    inp.ids[5, 1] = w.E + 3
+    inp.ids[77, 0] = -1
+    layer, _ = run(inp, ids_dtype=np.int32)
+    ref = _full_check(inp, layer)
+    ds = layer.dscores.cpu().numpy()
+    assert ds[5, 1] == 0 and ds[77, 0] == 0 and ref["bad"] == 2
+
+
+def test_forward_without_save_matches_saving_forward():
+    _, dv = _lib()
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_ragged"])
+    l1, _ = run(inp, backward=False, save=True)
+    l2, _ = run(inp, backward=False, save=False)
+    np.testing.assert_array_equal(dv.to_host_bits(l1.out), dv.to_host_bits(l2.out))
+
+
+def test_repeated_calls_are_bitwise_identical():
+    _, dv = _lib()
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_skew"])
+    l1, d = run(inp)
+    outs = [dv.to_host_bits(t) for t in (l1.out, l1.dx, l1.dw13, l1.dw2)] + [
+        l1.dscores.cpu().numpy()]
+    l1.plan(d["ids"])
+    l1.forward(d["x"], d["scores"], d["w13"], d["w2"])
+    l1.backward(d["dout"], d["scores"], d["w13"], d["w2"])
+    torch.cuda.synchronize()
+    again = [dv.to_host_bits(t) for t in (l1.out, l1.dx, l1.dw13, l1.dw2)] + [
+        l1.dscores.cpu().numpy()]
+    for a, b in zip(outs, again):
+        np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------------
+# full-size workloads, sampled
+
+_cache = {}
+
+
+def _large(name):
+    if name in _cache:
+        return _cache[name]
+    _cache.clear()
+    _, dv = _lib()
+    w = W.WORKLOADS[name]
+    t0 = time.time()
+    inp = W.make_inputs(w, with_dout=True)
+    log("\n[%s] inputs drawn in %.1fs" % (name, time.time() - t0))
+    layer, d = run(inp, backward=True, save=True)
+    log("[%s] gpu forward+backward done" % name)
+    _cache[name] = (inp, layer)
+    return _cache[name]
+
+
+LARGE = ["fine_grained", "large_hidden", "imbalanced", "training"]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_plan_and_permute_in_full(name):
+    inp, layer = _large(name)
+    w = inp.w
+    pl = plan_check(layer, inp.ids, w.E)
+    sv = layer.saved_arrays()
+    np.testing.assert_array_equal(sv["xg"], inp.x[pl["src"] // w.K])
+
+
+@pytest.mark.parametrize("half", [0, 1])
+@pytest.mark.parametrize("name", LARGE)
+def test_large_sampled_tokens(name, half):
+    _, dv = _lib()
+    inp, layer = _large(name)
+    w = inp.w
+    toks = W.sample_tokens(w.T, 256, seed=1)[half * 128:(half + 1) * 128]
+    t0 = time.time()
+    ref = oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks, inp.dout)
+    log("\n[%s] oracle on %d tokens: %.1fs" % (name, len(toks), time.time() - t0))
+    assert_close("out", dv.bits_to_f64(dv.to_host_bits(layer.out))[toks], ref["out"])
+    assert_close("dscores", layer.dscores.cpu().numpy()[toks], ref["dscores"])
+    assert_close("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx))[toks], ref["dx"])
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_sampled_weight_grads(name):
+    _, dv = _lib()
+    inp, layer = _large(name)
+    w = inp.w
+    counts = oracle.plan(inp.ids, w.E)["counts"]
+    rng = np.random.default_rng(17)
+    experts = [int(np.argmax(counts)), int(np.argmin(counts))]
+    others = [e for e in range(w.E) if e not in experts]
+    experts += [int(e) for e in rng.choice(others, 2, replace=False)]
+    dw13 = dv.to_host_bits(layer.dw13).reshape(w.E, 2 * w.F, w.D)
+    dw2 = dv.to_host_bits(layer.dw2)
+    t0 = time.time()
+    for i, e in enumerate(experts):
+        jd = W.sample_pairs(2 * w.F, w.D, 48, 1, 100 + i)
+        df = W.sample_pairs(w.D, w.F, 48, 1, 200 + i)
+        v13, v2 = oracle.wgrad_entries(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e,
+                                       jd, df)
+        log("\n[%s] expert %d (%d rows)" % (name, e, counts[e]))
+        assert_close("dw13", dv.bits_to_f64(dw13[e][jd[:, 0], jd[:, 1]]), v13)
+        assert_close("dw2", dv.bits_to_f64(dw2[e][df[:, 0], df[:, 1]]), v2)
+    log("[%s] oracle weight-grad entries: %.1fs" % (name, time.time() - t0))
