@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--workload", default="large_hidden")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=256,
                     help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a reference kernel of "
+                         "known traffic for hardware-counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is one GPU's share of an "
@@ -140,6 +143,15 @@ def main():
     log("bench: %s inputs drawn in %.1fs" % (w.name, time.time() - t0))
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src_buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)  # reads and writes exactly n bytes
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+        log("bench: copy probe of %d MiB done" % args.copy_probe_mib)
     x, w13, w2, dout = (dv.to_device_bits(a) for a in (inp.x, inp.w13, inp.w2, inp.dout))
     ids = torch.from_numpy(inp.ids).cuda()
     scores = torch.from_numpy(inp.scores).cuda()

@@ -45,7 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;
+constexpr int kBK = 64;  // k per LDS stage
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;
 
@@ -76,7 +76,20 @@ struct GemmArgs {
   const int32_t* lpt;          // SCHED_KSEG: experts by decreasing row count
 };
 
-__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row ^ (row >> 3)) & 7); }
+// LDS tile layout: [rows][BK] bf16, each row BK/8 chunks of 16 bytes; logical chunk c of row r
+// is stored at physical chunk c ^ t(r):
+//   BK = 64 (8 chunks, 128-byte rows): t(r) = (r ^ r>>3) & 7
+//   BK = 32 (4 chunks, 64-byte rows):  t(r) = (r>>1 ^ r>>3) & 3
+// With these, a fragment read (32 consecutive rows at one chunk) and the tile writes touch every
+// LDS bank at most once in each 8-lane (32-bank) or 16-lane (64-bank) phase.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int ch) {
+  if constexpr (BK == 64)
+    return ch ^ ((row ^ (row >> 3)) & 7);
+  else
+    return ch ^ (((row >> 1) ^ (row >> 3)) & 3);
+}
+
 
 struct Tile {
   int e, r0, r_lim, n0, kbeg, kend;
@@ -127,139 +140,174 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
 
 // ---- operand tiles ---------------------------------------------------------------------------
 
-// k-contiguous operand: R rows of 64 k; thread copies R/32 chunks of 16 bytes per k step.
+// One 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4, scalar base + 32-bit lane
+// offset): lane l's 16 bytes land at LDS byte address lds + 16*l. Issued through inline assembly
+// so that the compiler's wait-count bookkeeping sees only the LDS reads of the MFMA loop (an
+// LDS-DMA it knows about makes it wait for every outstanding LDS read); the copies are waited for
+// explicitly (s_waitcnt 0) before each barrier. M0 carries the LDS address; the kernels that use
+// this have no other use of M0.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, const uint16_t* lds) {
+  typedef __attribute__((address_space(3))) const uint16_t* lds_ptr;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// k-contiguous operand, copied global -> LDS by DMA: one instruction moves 64 lanes x 16 bytes
+// into 1 KiB of LDS, i.e. 8 rows x 64 k of the tile with lane l landing in row l/8, physical
+// chunk l%8. Each lane therefore fetches the logical chunk that the swizzle stores there. The R/8
+// blocks of a tile are split evenly over the 4 wavefronts (R/32 each). Addresses: a wave-uniform
+// base plus a 32-bit byte offset per lane and block.
 template <int R>
-struct KcTile {
-  static constexpr int IT = R / 32;
-  const uint16_t* src[IT];
-  int dst[IT];  // LDS element offset
-  uint4 v[IT];
+struct DmaTile {
+  static constexpr int NB = R / 32;  // blocks per wavefront = copy actions per stage
+  const char* base;                  // uniform
+  uint32_t off[NB];                  // per lane, bytes from base (k = 0)
 
-  __device__ __forceinline__ void init_row(int it, const uint16_t* rowptr) {
-    const int row = it * 32 + (threadIdx.x >> 3), ch = threadIdx.x & 7;
-    src[it] = rowptr + ch * 8;
-    dst[it] = row * kBK + swz(row, ch) * 8;
-  }
-  __device__ __forceinline__ static int row_of(int it) { return it * 32 + (threadIdx.x >> 3); }
-  __device__ __forceinline__ void load(int k0) {
+  // row_off(row) -> byte offset of the start of tile row `row` (0 <= row < R) from base
+  template <typename RowOff>
+  __device__ __forceinline__ void init(const void* b, RowOff row_off) {
+    base = uniform_ptr(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) v[it] = *(const uint4*)(src[it] + k0);
+    for (int i = 0; i < NB; ++i) {
+      const int blk = wave * NB + i;
+      const int row = blk * 8 + (lane >> 3);
+      off[i] = row_off(row) + swz<kBK>(row, lane & 7) * 16;
+    }
   }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-#pragma unroll
-    for (int it = 0; it < IT; ++it) *(uint4*)(s + dst[it]) = v[it];
+  __device__ __forceinline__ void issue(const uint16_t* lds_tile, int k0, int i) const {
+    const int blk = (threadIdx.x >> 6) * NB + i;
+    dma16(base + (int64_t)k0 * 2, off[i], lds_tile + blk * 8 * kBK);
   }
 };
 
-// idx-contiguous operand: tile of R idx x 64 k read as R 8x8 blocks (one per thread, threads < R).
-template <int R, bool MASK_K>
-struct McTile {
-  const uint16_t* base;  // points at (k = 0, idx = this thread's first idx)
-  int64_t ld;
-  int kb;  // this thread's 8-row k block
-  int ib;  // this thread's 8-wide idx block
-  int kend;
-  bool active;
-  uint4 v[8];
+// idx-contiguous operand ([k][idx] in memory): the tile is kept in that orientation in LDS,
+// [64 k][R idx] with 512-byte rows for R = 256, and turned into MFMA fragments by the LDS transpose
+// read (ds_read_b64_tr_b16). Copy: 1 KiB DMA blocks of 2 k rows; lane l lands in row l/32 at
+// physical 16-byte chunk l%32 and fetches the logical chunk stored there. Layout: the 8-byte chunk
+// x of row k sits at x ^ ((k & 3) << 3), which keeps the transpose reads (4 rows x 8 chunks per
+// 32 lanes) on distinct banks and keeps each lane's 16-byte DMA chunk contiguous.
+// Rows past kend (ragged reduction of a weight gradient) are clamped to row kend-1 here and
+// zeroed in the P fragments (mask_tail in the kernel), so every product past kend is 0.
+template <int R>
+struct MnTile {
+  static constexpr int NB = 64 / 2 / 4;  // 1 KiB blocks per wavefront (8)
+  static_assert(R == 256, "MN tiles are 256 wide");
+  const char* base;   // uniform: element (k = kbeg, idx = 0 of the tile's idx range)
+  int64_t ldb;        // bytes between k rows
+  uint32_t col[NB];   // per lane: byte offset of its 16-byte chunk within a row (clamped)
+  int row[NB];        // per lane: k row within a stage (0..63)
 
-  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld_, int idx0, int idx_lim,
-                                       int kend_) {
-    const int tid = threadIdx.x;
-    active = tid < R;
-    ib = tid % (R / 8);
-    kb = tid / (R / 8);
-    int idx = idx0 + ib * 8;
-    if (idx > idx_lim - 8) idx = idx_lim - 8;
-    base = b + idx;
-    ld = ld_;
-    kend = kend_;
-  }
-  __device__ __forceinline__ void load(int k0) {
-    if (!active) return;
+  __device__ __forceinline__ void init(const void* b, int64_t ld, int idx0, int idx_lim) {
+    base = uniform_ptr(b);
+    ldb = ld * 2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = k0 + kb * 8 + kk;
-      if (MASK_K && k >= kend)
-        v[kk] = make_uint4(0, 0, 0, 0);
-      else
-        v[kk] = *(const uint4*)(base + (int64_t)k * ld);
+    for (int i = 0; i < NB; ++i) {
+      const int blk = wave * NB + i;
+      const int k = blk * 2 + (lane >> 5);
+      const int logical = (lane & 31) ^ ((k & 3) << 2);  // 16-byte chunk within the row
+      int idx = idx0 + logical * 8;
+      if (idx > idx_lim - 8) idx = idx_lim - 8;
+      col[i] = (uint32_t)(idx * 2);
+      row[i] = k;
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    if (!active) return;
-    const uint32_t* w = (const uint32_t*)v;  // w[kk*4 + q]: idx pair (2q, 2q+1) at row kk
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = w[(2 * q) * 4 + (i >> 1)], hi = w[(2 * q + 1) * 4 + (i >> 1)];
-        o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      const int row = ib * 8 + i;
-      *(uint4*)(s + row * kBK + swz(row, kb) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+  // copy k rows [k0, k0+64) of the tile (k counted from kbeg); rows at or past klim (relative
+  // count of valid rows) are clamped to klim - 1
+  __device__ __forceinline__ void issue(const uint16_t* lds_tile, int k0, int klim, int i) const {
+    const int blk = (threadIdx.x >> 6) * NB + i;
+    int k = k0 + row[i];
+    if (k > klim - 1) k = klim - 1;  // k0 <= klim - 1 whenever the stage exists
+    dma16(base + (int64_t)k0 * ldb, (uint32_t)((k - k0) * ldb) + col[i], lds_tile + blk * 2 * R);
   }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// Half h (k 4h..4h+3 of each 8) of the MFMA fragment of a [64][256] MN tile for the 32 idx
+// starting at idx0 and k sub-step ks: lane l receives idx idx0 + (l & 31), k rows
+// 16 ks + 8 (l >> 5) + 4 h + 0..3. Within each 16-lane group, lane 4q + p points at row q,
+// idx chunk p of the 16 the group covers.
+__device__ __forceinline__ v4i16 read_mn_half(const uint16_t* tile, int idx0, int ks, int h) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int k = ks * 16 + (g >> 1) * 8 + h * 4 + (j >> 2);
+  const int x = ((idx0 + (g & 1) * 16) >> 2) + (j & 3);  // 8-byte chunk
+  const int xp = x ^ ((k & 3) << 3);
+  const lds_u16* p = (const lds_u16*)(tile) + k * 256 + xp * 4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
 
 // ---- the kernel -------------------------------------------------------------------------------
 
 template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(
-    GemmArgs g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  static_assert(FM >= 1 && FN >= 2 && (FN % 2) == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * kBK];
+  static_assert(BM == 256 && BN == 256, "the interleaved schedule below assumes 256x256 tiles");
+  constexpr int BK = kBK;
+  constexpr bool MASK_K = SCHED == SCHED_KSEG;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (BM + BN) * BK];
 
   Tile t;
   if (!decode_tile<BM, BN, SCHED, EPI>(g, t)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave & 1, wc = wave >> 1;
+  const int klen = t.kend - t.kbeg;
 
   // operand P (rows of the output)
-  KcTile<BM> pk;
-  McTile<BM, SCHED == SCHED_KSEG> pm;
+  DmaTile<BM> pd;
+  MnTile<BM> pm;
   if constexpr (P_KC) {
-#pragma unroll
-    for (int it = 0; it < BM / 32; ++it) {
-      int r = t.r0 + KcTile<BM>::row_of(it);
-      if (r > t.r_lim - 1) r = t.r_lim - 1;
-      pk.init_row(it, g.P + (int64_t)r * g.ldp);
-    }
+    const int r0 = t.r0, rl = t.r_lim;
+    const int64_t ldb = g.ldp * 2;
+    pd.init(g.P + (int64_t)r0 * g.ldp, [&](int row) -> uint32_t {
+      int r = r0 + row;
+      if (r > rl - 1) r = rl - 1;
+      return (uint32_t)((int64_t)(r - r0) * ldb);
+    });
   } else {
-    pm.init(g.P, g.ldp, t.r0, t.r_lim, t.kend);
+    pm.init(g.P + (int64_t)t.kbeg * g.ldp + t.r0, g.ldp, 0, t.r_lim - t.r0);
   }
   // operand Q (columns of the output)
   const uint16_t* qbase = g.Q + (int64_t)t.e * g.q_estride;
-  KcTile<BN> qk;
-  McTile<BN, SCHED == SCHED_KSEG> qm;
+  DmaTile<BN> qd;
+  MnTile<BN> qm;
   if constexpr (Q_KC) {
-#pragma unroll
-    for (int it = 0; it < BN / 32; ++it) {
-      const int c = KcTile<BN>::row_of(it);
+    const int n0 = t.n0, F = g.F, nlim = g.N_out;
+    const int64_t ldb = g.ldq * 2;
+    qd.init(qbase, [&](int c) -> uint32_t {
       int wrow;
       if constexpr (EPI == EPI_SWIGLU_FWD) {
         // tile column c -> wavefront column half, MFMA block, lane; the first FN/2 blocks of a
         // wavefront hold gate rows and the last FN/2 the up rows of the same f
         const int wq = c / WN, within = c % WN, blk = within / 32, ln = within % 32;
         const int half = blk / (FN / 2);
-        int f = t.n0 + wq * (WN / 2) + (blk % (FN / 2)) * 32 + ln;
-        if (f > g.F - 1) f = g.F - 1;
-        wrow = half * g.F + f;
+        int f = n0 + wq * (WN / 2) + (blk % (FN / 2)) * 32 + ln;
+        if (f > F - 1) f = F - 1;
+        wrow = half * F + f;
       } else {
-        wrow = t.n0 + c;
-        if (wrow > g.N_out - 1) wrow = g.N_out - 1;
+        wrow = n0 + c;
+        if (wrow > nlim - 1) wrow = nlim - 1;
       }
-      qk.init_row(it, qbase + (int64_t)wrow * g.ldq);
-    }
+      return (uint32_t)((int64_t)wrow * ldb);
+    });
   } else {
-    qm.init(qbase, g.ldq, t.n0, g.N_out, t.kend);
+    qm.init(qbase + (int64_t)t.kbeg * g.ldq + t.n0, g.ldq, 0, g.N_out - t.n0);
   }
-
-  // buffer b: P tile at smem + b*(BM+BN)*64, Q tile right after it
-  auto sP = [&](int b) { return smem + b * (BM + BN) * kBK; };
-  auto sQ = [&](int b) { return smem + b * (BM + BN) * kBK + BM * kBK; };
 
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -269,48 +317,110 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  const int nk = (t.kend - t.kbeg + kBK - 1) / kBK;
+  const int nk = (klen + BK - 1) / BK;
+  auto bufP = [&](int b) { return lds + b * (BM + BN) * BK; };
+  auto bufQ = [&](int b) { return lds + b * (BM + BN) * BK + BM * BK; };
 
-  auto load = [&](int k0) {
-    if constexpr (P_KC) pk.load(k0); else pm.load(k0);
-    if constexpr (Q_KC) qk.load(k0); else qm.load(k0);
-  };
-  auto store = [&](int buf) {
-    if constexpr (P_KC) pk.store(sP(buf)); else pm.store(sP(buf));
-    if constexpr (Q_KC) qk.store(sQ(buf)); else qm.store(sQ(buf));
+  // copy of one stage: 8 DMA blocks per operand and wavefront
+  static_assert(DmaTile<BM>::NB == 8 && MnTile<BM>::NB == 8, "8 copies per operand");
+  auto copy_issue = [&](int b, int kt, int n) {
+    const int k0 = kt * BK;  // relative to kbeg
+    if (n < 8) {
+      if constexpr (P_KC) pd.issue(bufP(b), t.kbeg + k0, n); else pm.issue(bufP(b), k0, klen, n);
+    } else {
+      if constexpr (Q_KC) qd.issue(bufQ(b), t.kbeg + k0, n - 8); else qm.issue(bufQ(b), k0, klen, n - 8);
+    }
   };
 
-  if (nk > 0) {
-    load(t.kbeg);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load(t.kbeg + (kt + 1) * kBK);
-      const uint16_t* P_s = sP(cur);
-      const uint16_t* Q_s = sQ(cur);
-#pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
+  // LDS read operations of k sub-step ks: Q fragments then P fragments; a k-contiguous fragment
+  // is one 16-byte read, an MN fragment two transpose reads (halves)
+  constexpr int RQ = Q_KC ? FN : 2 * FN, RP = P_KC ? FM : 2 * FM, NR = RQ + RP;
+  static_assert(NR <= 16, "read slots");
+  bf16x8 qa[2][FN], pb[2][FM];
+  auto read_op = [&](int b, int ks, int n) {
+    if (n < RQ) {
+      if constexpr (Q_KC) {
+        const int row = wc * WN + n * 32 + (lane & 31);
         const int ch = ks * 2 + (lane >> 5);
-        bf16x8 qa[FN], pb[FM];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int row = wc * WN + i * 32 + (lane & 31);
-          qa[i] = *(const bf16x8*)(Q_s + row * kBK + swz(row, ch) * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int row = wr * WM + j * 32 + (lane & 31);
-          pb[j] = *(const bf16x8*)(P_s + row * kBK + swz(row, ch) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-          for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i], pb[j], acc[i][j], 0, 0, 0);
+        qa[ks & 1][n] = *(const bf16x8*)(bufQ(b) + row * BK + swz<BK>(row, ch) * 8);
+      } else {
+        const v4i16 h = read_mn_half(bufQ(b), wc * WN + (n >> 1) * 32, ks, n & 1);
+        v4i16* dst = (v4i16*)&qa[ks & 1][n >> 1];
+        dst[n & 1] = h;
       }
-      if (kt + 1 < nk) store(cur ^ 1);
-      __syncthreads();
+    } else {
+      const int m = n - RQ;
+      if constexpr (P_KC) {
+        const int row = wr * WM + m * 32 + (lane & 31);
+        const int ch = ks * 2 + (lane >> 5);
+        pb[ks & 1][m] = *(const bf16x8*)(bufP(b) + row * BK + swz<BK>(row, ch) * 8);
+      } else {
+        const v4i16 h = read_mn_half(bufP(b), wr * WM + (m >> 1) * 32, ks, m & 1);
+        v4i16* dst = (v4i16*)&pb[ks & 1][m >> 1];
+        dst[m & 1] = h;
+      }
+    }
+  };
+  // ragged reduction: in the last stage, zero the P-fragment k elements at or past the segment
+  // end (the copies clamp those rows to the last valid row, so both operands hold finite data)
+  auto mask_tail = [&](int kt, int ks) {
+    if constexpr (MASK_K) {
+      const int kfirst = kt * BK + ks * 16 + 8 * (lane >> 5);
+      if (kt * BK + BK > klen) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (kfirst + e >= klen) pb[ks & 1][j][e] = (__bf16)0.0f;
+      }
+    }
+  };
+
+  // Schedule of one stage (64 MFMAs: m = 0..15 in each of the 4 k sub-steps ks): with one
+  // wavefront per SIMD the matrix unit only stays busy if every other instruction slips in
+  // between MFMAs, so after MFMA (ks, m):
+  //   ks < 3:              the LDS read operations of sub-step ks+1, spread over the 16 slots
+  //   ks < 2, m odd:       one DMA copy of the next stage (into the other buffer)
+  //   before (3, 12):      wait for this wave's copies, barrier: every wave's copies of the next
+  //                        stage have landed, and this buffer is no longer read after this point
+  //   ks = 3, m >= 12:     the read operations of sub-step 0 of the next stage
+  // The buffer written during stage s was last read before the barrier of stage s-1.
+  if (nk > 0) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n) copy_issue(0, 0, n);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NR; ++n) read_op(0, 0, n);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1, nxt = cur ^ 1;
+      const bool more = kt + 1 < nk;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        mask_tail(kt, ks);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          if (ks == 3 && m == 12) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              qa[ks & 1][m >> 2], pb[ks & 1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+          if (ks < 3) {
+#pragma unroll
+            for (int n = (m * NR) / 16; n < ((m + 1) * NR) / 16; ++n) read_op(cur, ks + 1, n);
+          }
+          if (more) {
+            if (ks < 2 && (m & 1) == 1) copy_issue(nxt, kt + 1, ks * 8 + (m >> 1));
+            if (ks == 3 && m >= 12) {
+#pragma unroll
+              for (int n = ((m - 12) * NR) / 4; n < ((m - 11) * NR) / 4; ++n) read_op(nxt, 0, n);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   }
 
@@ -396,15 +506,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI>
-hipError_t launch(const GemmArgs& g, int grid, hipStream_t st) {
+constexpr int kBM = 256, kBN = 256;
+
+#define MOE_GEMM_KERNEL(name, P_KC, Q_KC, SCHED, EPI)                                          \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void name( \
+      GemmArgs g) {                                                                            \
+    gemm_body<kBM, kBN, P_KC, Q_KC, SCHED, EPI>(g);                                            \
+  }
+
+MOE_GEMM_KERNEL(moe_fprop_w13_swiglu, true, true, SCHED_ROWS, EPI_SWIGLU_FWD)
+MOE_GEMM_KERNEL(moe_fprop_w2, true, true, SCHED_ROWS, EPI_STORE)
+MOE_GEMM_KERNEL(moe_dgrad_w2_swiglu, true, false, SCHED_ROWS, EPI_SWIGLU_BWD)
+MOE_GEMM_KERNEL(moe_dgrad_w13, true, false, SCHED_ROWS, EPI_STORE)
+MOE_GEMM_KERNEL(moe_wgrad_w2, false, false, SCHED_KSEG, EPI_STORE)
+MOE_GEMM_KERNEL(moe_wgrad_w13, false, false, SCHED_KSEG, EPI_STORE)
+
+hipError_t launch(void (*kernel)(GemmArgs), const GemmArgs& g, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<BM, BN, P_KC, Q_KC, SCHED, EPI>), dim3(grid), dim3(kThreads), 0, st,
-                     g);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
-
-constexpr int kBM = 256, kBN = 256;
 
 GemmArgs rows_args(const moe_shape& s, const PlanPtrs& p, int bm) {
   GemmArgs g{};
@@ -433,7 +554,7 @@ hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   g.C2 = a; g.ldc2 = s.F;
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
   const int ntn = (int)ceil_div(s.F, kBN / 2);
-  return launch<kBM, kBN, true, true, SCHED_ROWS, EPI_SWIGLU_FWD>(g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_fprop_w13_swiglu, g, rows_grid(s, kBM, ntn), st);
 }
 
 hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
@@ -444,7 +565,7 @@ hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
   g.C = y; g.ldc = s.D;
   g.N_out = (int)s.D; g.Kdim = (int)s.F;
   const int ntn = (int)ceil_div(s.D, kBN);
-  return launch<kBM, kBN, true, true, SCHED_ROWS, EPI_STORE>(g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_fprop_w2, g, rows_grid(s, kBM, ntn), st);
 }
 
 hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
@@ -457,7 +578,7 @@ hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
   g.H = h13; g.ldh = 2 * s.F;
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
   const int ntn = (int)ceil_div(s.F, kBN);
-  return launch<kBM, kBN, true, false, SCHED_ROWS, EPI_SWIGLU_BWD>(g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_dgrad_w2_swiglu, g, rows_grid(s, kBM, ntn), st);
 }
 
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
@@ -468,7 +589,7 @@ hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   g.C = dxg; g.ldc = s.D;
   g.N_out = (int)s.D; g.Kdim = (int)(2 * s.F);
   const int ntn = (int)ceil_div(s.D, kBN);
-  return launch<kBM, kBN, true, false, SCHED_ROWS, EPI_STORE>(g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_dgrad_w13, g, rows_grid(s, kBM, ntn), st);
 }
 
 hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
@@ -480,7 +601,7 @@ hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
   g.C = dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
   g.M_out = (int)s.D; g.N_out = (int)s.F;
   const int grid = (int)(s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN));
-  return launch<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE>(g, grid, st);
+  return launch(moe_wgrad_w2, g, grid, st);
 }
 
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
@@ -492,7 +613,7 @@ hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   g.C = dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
   g.M_out = (int)(2 * s.F); g.N_out = (int)s.D;
   const int grid = (int)(s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN));
-  return launch<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE>(g, grid, st);
+  return launch(moe_wgrad_w13, g, grid, st);
 }
 
 }  // namespace moe

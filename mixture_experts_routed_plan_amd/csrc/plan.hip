@@ -5,11 +5,11 @@
 // per-expert compute batches -- here the per-expert row-tile lists the grouped GEMMs walk.
 //
 // Three launches, all sized by the shape only (nothing is read back to the host):
-//   1. k_plan_hist    one wavefront per chunk of kPlanChunk slots: expert histogram in LDS.
-//   2. k_plan_scan    one workgroup: per-expert scan over chunks (chunk bases), counts, the
+//   1. moe_plan_hist    one wavefront per chunk of kPlanChunk slots: expert histogram in LDS.
+//   2. moe_plan_scan    one workgroup: per-expert scan over chunks (chunk bases), counts, the
 //                     exclusive scan of counts (offsets), row-tile lists for 64/128/256-row
 //                     tiles, the expert order by decreasing count, the out-of-range total.
-//   3. k_plan_scatter one wavefront per chunk, slots in ascending order, 64 at a time: lanes that
+//   3. moe_plan_scatter one wavefront per chunk, slots in ascending order, 64 at a time: lanes that
 //                     share an expert id find each other with one ballot per id bit, take
 //                     consecutive rows after the expert's running base in lane order, and the
 //                     lowest such lane advances the base. This keeps the order of equal ids
@@ -26,7 +26,7 @@ __device__ __forceinline__ int load_expert(const IdT* ids, int i, int E) {
 }
 
 template <typename IdT>
-__global__ __launch_bounds__(64) void k_plan_hist(const IdT* __restrict__ ids, int N, int E,
+__global__ __launch_bounds__(64) void moe_plan_hist(const IdT* __restrict__ ids, int N, int E,
                                                   int NB, int32_t* __restrict__ blkhist,
                                                   int32_t* __restrict__ blkbad) {
   __shared__ int32_t h[MOE_MAX_EXPERTS];
@@ -71,7 +71,7 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wsum) {
   return v + add;
 }
 
-__global__ __launch_bounds__(1024) void k_plan_scan(int N, int E, int NB, int32_t* status,
+__global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int32_t* status,
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* blkhist, const int32_t* blkbad,
                                                     int32_t* lpt, int32_t* src, int32_t* mt64,
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int N, int E, int NB, int32_
 }
 
 template <typename IdT>
-__global__ __launch_bounds__(64) void k_plan_scatter(const IdT* __restrict__ ids, int N, int E,
+__global__ __launch_bounds__(64) void moe_plan_scatter(const IdT* __restrict__ ids, int N, int E,
                                                      int NB, int nbits,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ blkhist,
@@ -179,17 +179,17 @@ hipError_t launch_plan_hist(const moe_shape& s, const PlanLayout& L, const PlanP
                             const void* ids, hipStream_t st) {
   const int N = (int)L.N, E = (int)s.E, NB = (int)L.NB;
   if (s.ids_dtype == MOE_IDS_I64)
-    hipLaunchKernelGGL(k_plan_hist<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids, N,
+    hipLaunchKernelGGL(moe_plan_hist<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids, N,
                        E, NB, p.blkhist, p.blkbad);
   else
-    hipLaunchKernelGGL(k_plan_hist<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids, N,
+    hipLaunchKernelGGL(moe_plan_hist<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids, N,
                        E, NB, p.blkhist, p.blkbad);
   return hipGetLastError();
 }
 
 hipError_t launch_plan_scan(const moe_shape& s, const PlanLayout& L, const PlanPtrs& p,
                             hipStream_t st) {
-  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, (int)L.N, (int)s.E, (int)L.NB,
+  hipLaunchKernelGGL(moe_plan_scan, dim3(1), dim3(1024), 0, st, (int)L.N, (int)s.E, (int)L.NB,
                      p.status, p.counts, p.offsets, p.blkhist, p.blkbad, p.lpt, p.src,
                      p.mtiles[0], p.mtiles[1], p.mtiles[2]);
   return hipGetLastError();
@@ -201,10 +201,10 @@ hipError_t launch_plan_scatter(const moe_shape& s, const PlanLayout& L, const Pl
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   if (s.ids_dtype == MOE_IDS_I64)
-    hipLaunchKernelGGL(k_plan_scatter<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids,
+    hipLaunchKernelGGL(moe_plan_scatter<int64_t>, dim3(NB), dim3(64), 0, st, (const int64_t*)ids,
                        N, E, NB, nbits, p.offsets, p.blkhist, p.pos, p.src);
   else
-    hipLaunchKernelGGL(k_plan_scatter<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids,
+    hipLaunchKernelGGL(moe_plan_scatter<int32_t>, dim3(NB), dim3(64), 0, st, (const int32_t*)ids,
                        N, E, NB, nbits, p.offsets, p.blkhist, p.pos, p.src);
   return hipGetLastError();
 }

@@ -31,7 +31,7 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
-__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
+__global__ __launch_bounds__(256) void moe_permute(const uint4* __restrict__ x,
                                                  const int32_t* __restrict__ pos,
                                                  uint4* __restrict__ xg, int T, int K, int nch) {
   const int lane = threadIdx.x & 63;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
 }
 
 template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ rows,
+__global__ __launch_bounds__(256) void moe_combine(const uint4* __restrict__ rows,
                                                  const int32_t* __restrict__ pos,
                                                  const float* __restrict__ scores,
                                                  uint4* __restrict__ out, int T, int K, int nch) {
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ rows,
   }
 }
 
-__global__ __launch_bounds__(256) void k_combine_bwd(const uint4* __restrict__ dout,
+__global__ __launch_bounds__(256) void moe_combine_bwd_dscores(const uint4* __restrict__ dout,
                                                      const uint4* __restrict__ y,
                                                      const int32_t* __restrict__ pos,
                                                      const float* __restrict__ scores,
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const uint4* __restrict__ d
 hipError_t launch_permute(const moe_shape& s, const int32_t* pos, const uint16_t* x, uint16_t* xg,
                           hipStream_t st) {
   const int T = (int)s.T;
-  hipLaunchKernelGGL(k_permute, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
+  hipLaunchKernelGGL(moe_permute, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
                      (const uint4*)x, pos, (uint4*)xg, T, (int)s.K, (int)(s.D / 8));
   return hipGetLastError();
 }
@@ -156,10 +156,10 @@ hipError_t launch_combine(const moe_shape& s, const int32_t* pos, const uint16_t
   const int T = (int)s.T;
   const dim3 grid((T + kRowWaves - 1) / kRowWaves);
   if (scores)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
+    hipLaunchKernelGGL(moe_combine<true>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
                        (uint4*)out, T, (int)s.K, (int)(s.D / 8));
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
+    hipLaunchKernelGGL(moe_combine<false>, grid, dim3(256), 0, st, (const uint4*)rows, pos, scores,
                        (uint4*)out, T, (int)s.K, (int)(s.D / 8));
   return hipGetLastError();
 }
@@ -168,7 +168,7 @@ hipError_t launch_combine_bwd(const moe_shape& s, const int32_t* pos, const uint
                               const uint16_t* y, const float* scores, uint16_t* dy,
                               float* dscores, hipStream_t st) {
   const int T = (int)s.T;
-  hipLaunchKernelGGL(k_combine_bwd, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
+  hipLaunchKernelGGL(moe_combine_bwd_dscores, dim3((T + kRowWaves - 1) / kRowWaves), dim3(256), 0, st,
                      (const uint4*)dout, (const uint4*)y, pos, scores, (uint4*)dy, dscores, T,
                      (int)s.K, (int)(s.D / 8));
   return hipGetLastError();
