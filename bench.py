@@ -112,18 +112,155 @@ def cpu_baseline(inp, n_tokens):
     }
 
 
+# ------------------------------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/) and the traffic figure read back from them
+
+SRC_FILES = ["mixture_experts_routed_plan_amd/csrc/gemm.hip",
+             "mixture_experts_routed_plan_amd/csrc/rowops.hip",
+             "mixture_experts_routed_plan_amd/csrc/plan.hip",
+             "mixture_experts_routed_plan_amd/csrc/moe_internal.h"]
+STAGE_KERNEL = {
+    "plan_hist": "moe_plan_hist", "plan_scan": "moe_plan_scan", "plan_scatter": "moe_plan_scatter",
+    "permute": "moe_permute", "fprop_w13_swiglu": "moe_fprop_w13_swiglu",
+    "fprop_w2": "moe_fprop_w2", "combine": "moe_combine<true>",
+    "combine_bwd_dscores": "moe_combine_bwd_dscores", "dgrad_w2_swiglu": "moe_dgrad_w2_swiglu",
+    "wgrad_w2": "moe_wgrad_w2", "dgrad_w13": "moe_dgrad_w13", "wgrad_w13": "moe_wgrad_w13",
+    "dx_combine": "moe_combine<false>",
+}
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SRC_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short_kernel(name):
+    import re
+    n = re.sub(r"^void ", "", name).replace("moe::(anonymous namespace)::", "")
+    n = re.sub(r"\((?!anonymous).*$", "", n)
+    return n.strip()
+
+
+def _counter_means(path):
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        acc[_short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def summarize(prof_dir, out_path, workload, cmd):
+    """Write a profile summary (markdown + one machine-readable JSON line) from a rocprofv3 run
+    directory holding trace/ (--kernel-trace --stats), fetch/ (FETCH_SIZE), write/ (WRITE_SIZE),
+    sq/ and tcc/ counter passes."""
+    import csv
+    stats = {}
+    for r in csv.DictReader(open(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))):
+        stats[_short_kernel(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                                          float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+    fetch = _counter_means(os.path.join(prof_dir, "fetch", "run_counter_collection.csv"))
+    write = _counter_means(os.path.join(prof_dir, "write", "run_counter_collection.csv"))
+    sq = _counter_means(os.path.join(prof_dir, "sq", "run_counter_collection.csv"))
+    tcc = _counter_means(os.path.join(prof_dir, "tcc", "run_counter_collection.csv"))
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy probe kernel in the counter runs (run bench.py with --copy-probe-mib)")
+    probe_kib = float(open(os.path.join(prof_dir, "probe_mib")).read()) * 1024 if os.path.exists(
+        os.path.join(prof_dir, "probe_mib")) else 1024 * 1024
+    f_fac = probe_kib / fetch[copy[0]]["FETCH_SIZE"]
+    w_fac = probe_kib / write[copy[0]]["WRITE_SIZE"]
+    rows = []
+    table = {}
+    for k, (calls, avg, mn, mx) in sorted(stats.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        if not k.startswith("moe_"):
+            continue
+        fk = fetch.get(k, {}).get("FETCH_SIZE")
+        wk = write.get(k, {}).get("WRITE_SIZE")
+        tb = (fk * f_fac + wk * w_fac) * 1024 if fk is not None and wk is not None else None
+        q = sq.get(k, {})
+        util = (q["SQ_VALU_MFMA_BUSY_CYCLES"] / (q["GRBM_GUI_ACTIVE"] / 8 * 1024)
+                if q.get("GRBM_GUI_ACTIVE") else None)
+        c = tcc.get(k, {})
+        hit = (c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+               if c.get("TCC_HIT_sum") is not None and (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]) > 0
+               else None)
+        table[k] = {"avg_us": round(avg, 2), "calls": calls, "traffic_bytes": tb,
+                    "fetch_kib_raw": fk, "write_kib_raw": wk, "mfma_busy": util, "l2_hit": hit}
+        rows.append("| %s | %d | %.1f | %.1f | %.1f | %s | %s | %s | %s |" % (
+            k, calls, avg, mn, mx,
+            "%.0f" % fk if fk is not None else "-", "%.0f" % wk if wk is not None else "-",
+            "%.3f" % (tb / 1e9) if tb is not None else "-",
+            ("%.2f / %.2f" % (util, hit)) if util is not None and hit is not None else "-"))
+    meta = {"workload": workload, "source_digest": source_digest(), "fetch_factor": f_fac,
+            "write_factor": w_fac, "kernels": table}
+    lines = [
+        "# Kernel profile: %s workload, plan + forward + backward" % workload, "",
+        "Made with rocprofv3 on one MI355X (gfx950: 256 CUs, 1024 SIMDs, 8 XCDs, 2400 MHz max "
+        "engine clock) from the repository root, five timed steps after one warm-up step:", "",
+        "```",
+        *cmd, "```", "",
+        "and summarized with `python bench.py --summarize <run dir> <this file>`.", "",
+        "Traffic calibration: the run starts with a plain 1 GiB device copy (`--copy-probe-mib "
+        "1024`, runtime kernel `__amd_rocclr_copyBuffer`), which reads and writes exactly "
+        "1048576 KiB. On it FETCH_SIZE reads %.0f KiB and WRITE_SIZE %.0f KiB, so HBM-side "
+        "traffic = %.3f x FETCH_SIZE + %.3f x WRITE_SIZE (KiB per dispatch)."
+        % (fetch[copy[0]]["FETCH_SIZE"], write[copy[0]]["WRITE_SIZE"], f_fac, w_fac), "",
+        "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+        "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS). Counter runs serialize kernels, so their "
+        "durations are not used; the times come from the kernel-trace run.", "",
+        "| kernel | calls | avg us | min us | max us | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+        "traffic GB | MFMA busy / L2 hit |",
+        "|---|---|---|---|---|---|---|---|---|",
+        *rows, "",
+        "Source digest of the kernels profiled (sha256 of the csrc files, first 16 hex digits): "
+        "`%s`" % meta["source_digest"], "",
+        "<!-- machine-readable -->",
+        "    " + json.dumps(meta), ""]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", out_path)
+
+
+def profiled_traffic(workload, kernel_short):
+    """HBM bytes per launch of `kernel_short` from profiles/, or None when absent or stale."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("{") and '"source_digest"' in line:
+                meta = json.loads(line)
+                if meta.get("workload") != workload or meta.get("source_digest") != source_digest():
+                    continue
+                ent = meta["kernels"].get(kernel_short)
+                if ent and ent.get("traffic_bytes"):
+                    return ent["traffic_bytes"]
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large_hidden")
-    ap.add_argument("--cpu-baseline-tokens", type=int, default=256,
+    ap.add_argument("--cpu-baseline-tokens", type=int, default=512,
                     help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--summarize", nargs=2, metavar=("RUN_DIR", "OUT_MD"),
+                    help="write a profile summary from a rocprofv3 run directory and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a reference kernel of "
                          "known traffic for hardware-counter runs)")
     args = ap.parse_args()
+    if args.summarize:
+        cmd_file = os.path.join(args.summarize[0], "commands.txt")
+        cmd = open(cmd_file).read().strip().splitlines() if os.path.exists(cmd_file) else []
+        summarize(args.summarize[0], args.summarize[1], args.workload, cmd)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is one GPU's share of an "
               "expert-parallel job and this build has no multi-GPU path (asked for --gpus %d)"
@@ -223,7 +360,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = profiled_traffic(w.name, STAGE_KERNEL[dom])
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
