@@ -44,8 +44,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;  // k per LDS stage
+constexpr int kEpWaveElems = 8704;  // per-wavefront epilogue staging area (bf16 elements)
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;
 
@@ -424,68 +426,116 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
   }
 
-  // ---- epilogue: lane holds rows r = base + (lane & 31), columns 8*gq + 4*(lane >> 5) + 0..3
-  const int cq = 4 * (lane >> 5);
+  // ---- epilogue ------------------------------------------------------------------------------
+  // Lane (lane&31, lane>>5) of the wavefront holds, for MFMA block (i, j), output row
+  // j*32 + (lane&31) of the wavefront's 128 rows and the 4 consecutive columns
+  // i*32 + 8*gq + 4*(lane>>5) + 0..3, gq = 0..3. Per 32-row block j the wavefront converts its
+  // values to bf16 (v_cvt_pk_bf16_f32, round to nearest even), parks them in a private LDS area
+  // with padded rows (the 8-byte writes of 32 rows land on distinct banks), reads them back as
+  // row segments and writes whole 16-byte chunks, 4 to 8 rows of contiguous bytes per
+  // instruction. The LDS stages are no longer read once every wavefront is past the loop.
+  __syncthreads();
+  const int cq = 4 * (lane >> 5), rl = lane & 31;
+  uint16_t* ep = lds + wave * kEpWaveElems;
+  auto pk2 = [](float a, float b) -> uint32_t {
+    bf16x2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  // read row segments of width W (bf16) out of a [32][W + 4] area and store them
+  auto flush = [&](const uint16_t* area, int W, uint16_t* dst, int64_t ld, int row0, int rlim,
+                   int col0, int clim) {
+    const int per_row = W / 8;            // 16-byte chunks per row
+    const int rows_per_pass = 64 / per_row;
+#pragma unroll
+    for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+      const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
+      const uint16_t* src = area + row * (W + 4) + ch * 8;
+      const uint2 lo = *(const uint2*)src, hi = *(const uint2*)(src + 4);
+      const int r = row0 + row, c = col0 + ch * 8;
+      if (r < rlim && c < clim)
+        *(uint4*)(dst + (int64_t)r * ld + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
   if constexpr (EPI == EPI_STORE) {
     uint16_t* C = g.C + (int64_t)t.e * g.c_estride;
+    constexpr int PW = WN + 4;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int r = t.r0 + wr * WM + j * 32 + (lane & 31);
-      if (r >= t.r_lim) continue;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int c = t.n0 + wc * WN + i * 32 + gq * 8 + cq;
-          if (c >= g.N_out) continue;
-          const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
-                                     pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]));
-          *(uint2*)(C + (int64_t)r * g.ldc + c) = v;
-        }
+        for (int gq = 0; gq < 4; ++gq)
+          *(uint2*)(ep + rl * PW + i * 32 + gq * 8 + cq) =
+              make_uint2(pk2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
+                         pk2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]));
+      flush(ep, WN, C, g.ldc, t.r0 + wr * WM + j * 32, t.r_lim, t.n0 + wc * WN, g.N_out);
     }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // the wavefront's 64 activation columns f0w .. f0w+63: a, g and u each through [32][68]
+    constexpr int W = WN / 2, PW = W + 4;
+    uint16_t* ea = ep;
+    uint16_t* eg = ep + 32 * PW;
+    uint16_t* eu = ep + 2 * 32 * PW;
+    const int f0w = t.n0 + wc * W;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int r = t.r0 + wr * WM + j * 32 + (lane & 31);
-      if (r >= t.r_lim) continue;
 #pragma unroll
       for (int i = 0; i < FN / 2; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int f = t.n0 + wc * (WN / 2) + i * 32 + gq * 8 + cq;
-          if (f >= g.F) continue;
-          uint32_t gb[4], ub[4];
-          float av[4];
+          float gv[4], uv[4], av[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            gb[q] = f32_to_bf16(acc[i][j][4 * gq + q]);
-            ub[q] = f32_to_bf16(acc[i + FN / 2][j][4 * gq + q]);
-            const float gv = bf16_to_f32(gb[q]), uv = bf16_to_f32(ub[q]);
-            av[q] = gv * sigmoid_f32(gv) * uv;
+            gv[q] = (float)(__bf16)acc[i][j][4 * gq + q];
+            uv[q] = (float)(__bf16)acc[i + FN / 2][j][4 * gq + q];
+            av[q] = gv[q] * sigmoid_f32(gv[q]) * uv[q];
           }
-          if (g.C) {
-            uint16_t* hrow = g.C + (int64_t)r * g.ldc;
-            *(uint2*)(hrow + f) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-            *(uint2*)(hrow + g.F + f) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
-          }
-          *(uint2*)(g.C2 + (int64_t)r * g.ldc2 + f) =
-              make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+          const int o = rl * PW + i * 32 + gq * 8 + cq;
+          *(uint2*)(eg + o) = make_uint2(pk2(gv[0], gv[1]), pk2(gv[2], gv[3]));
+          *(uint2*)(eu + o) = make_uint2(pk2(uv[0], uv[1]), pk2(uv[2], uv[3]));
+          *(uint2*)(ea + o) = make_uint2(pk2(av[0], av[1]), pk2(av[2], av[3]));
         }
+      const int row0 = t.r0 + wr * WM + j * 32;
+      flush(ea, W, g.C2, g.ldc2, row0, t.r_lim, f0w, g.F);
+      if (g.C) {
+        flush(eg, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
+        flush(eu, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
+      }
     }
-  } else {  // EPI_SWIGLU_BWD: acc = da over columns f
+  } else {  // EPI_SWIGLU_BWD: acc = da over columns f; g, u come from the saved h13
+    constexpr int PW = WN + 4;
+    uint16_t* e1 = ep;             // g, then dg
+    uint16_t* e2 = ep + 32 * PW;   // u, then du
+    const int f0w = t.n0 + wc * WN;
+    constexpr int per_row = WN / 8, rows_per_pass = 64 / per_row;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int r = t.r0 + wr * WM + j * 32 + (lane & 31);
-      if (r >= t.r_lim) continue;
+      const int row0 = t.r0 + wr * WM + j * 32;
+      // coalesced loads of the g and u row segments (rows past the segment clamped)
+#pragma unroll
+      for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+        const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
+        int r = row0 + row;
+        if (r > t.r_lim - 1) r = t.r_lim - 1;
+        int c = f0w + ch * 8;
+        if (c > g.F - 8) c = g.F - 8;
+        const uint16_t* hrow = g.H + (int64_t)r * g.ldh + c;
+        const uint4 gv = *(const uint4*)hrow, uv = *(const uint4*)(hrow + g.F);
+        uint16_t* d1 = e1 + row * PW + ch * 8;
+        uint16_t* d2 = e2 + row * PW + ch * 8;
+        *(uint2*)d1 = make_uint2(gv.x, gv.y);
+        *(uint2*)(d1 + 4) = make_uint2(gv.z, gv.w);
+        *(uint2*)d2 = make_uint2(uv.x, uv.y);
+        *(uint2*)(d2 + 4) = make_uint2(uv.z, uv.w);
+      }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int f = t.n0 + wc * WN + i * 32 + gq * 8 + cq;
-          if (f >= g.F) continue;
-          const uint16_t* hrow = g.H + (int64_t)r * g.ldh;
-          const uint2 gh = *(const uint2*)(hrow + f);
-          const uint2 uh = *(const uint2*)(hrow + g.F + f);
+          const int o = rl * PW + i * 32 + gq * 8 + cq;
+          const uint2 gh = *(const uint2*)(e1 + o), uh = *(const uint2*)(e2 + o);
           const uint32_t gw[4] = {gh.x & 0xffffu, gh.x >> 16, gh.y & 0xffffu, gh.y >> 16};
           const uint32_t uw[4] = {uh.x & 0xffffu, uh.x >> 16, uh.y & 0xffffu, uh.y >> 16};
           float dg[4], du[4];
@@ -497,11 +547,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             dg[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
             du[q] = da * gv * sg;
           }
-          uint16_t* drow = g.C + (int64_t)r * g.ldc;
-          *(uint2*)(drow + f) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *(uint2*)(drow + g.F + f) =
-              make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          *(uint2*)(e1 + o) = make_uint2(pk2(dg[0], dg[1]), pk2(dg[2], dg[3]));
+          *(uint2*)(e2 + o) = make_uint2(pk2(du[0], du[1]), pk2(du[2], du[3]));
         }
+      flush(e1, WN, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
+      flush(e2, WN, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
     }
   }
 }

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe_routed.h"
+#include "moe_routed.h"  // include/ is on the include path
 
 namespace moe {
 
