@@ -8,6 +8,7 @@
 //                results of one token reduced locally). With unit weights it is the dX reduction.
 //   combine_bwd  dy[pos[t,k]] = bf16(s[t,k] * dout[t]) and dscores[t,k] = <dout[t], y[pos[t,k]]>
 //                -- the transpose of combine and the derivative with respect to the scores.
+//                dout[t] is read once per group of 8 slots.
 //
 // One wavefront per token; every lane moves 16-byte chunks (8 bf16), so one wavefront instruction
 // touches 1 KiB of a row. The K slots of a token are wave-uniform (pos and scores come through
@@ -104,6 +105,9 @@ __global__ __launch_bounds__(256) void moe_combine(const uint4* __restrict__ row
   }
 }
 
+// One wavefront per token; the K slots are taken in groups of up to 8 so that each chunk of
+// dout[t] is read once per group (once in all for K <= 8) while the slots' y rows stream past it.
+// Per slot the dot product accumulates lane-wise over ascending chunks, then across the wavefront.
 __global__ __launch_bounds__(256) void moe_combine_bwd_dscores(const uint4* __restrict__ dout,
                                                      const uint4* __restrict__ y,
                                                      const int32_t* __restrict__ pos,
@@ -111,33 +115,44 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_dscores(const uint4* __re
                                                      uint4* __restrict__ dy,
                                                      float* __restrict__ dscores, int T, int K,
                                                      int nch) {
+  constexpr int KG = 8;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
   if (t >= T) return;
   const uint4* dr = dout + (int64_t)t * nch;
-  for (int k = 0; k < K; ++k) {
-    const int p = pos[(int64_t)t * K + k];
-    if (p < 0) {
-      if (lane == 0) dscores[(int64_t)t * K + k] = 0.0f;
-      continue;
-    }
-    const float s = scores[(int64_t)t * K + k];
-    const uint4* yr = y + (int64_t)p * nch;
-    uint4* dyr = dy + (int64_t)p * nch;
-    float part = 0.0f;
-    for (int c = lane; c < nch; c += 64) {
-      float fd[8], fy[8], o[8];
-      unpack8(dr[c], fd);
-      unpack8(yr[c], fy);
+  for (int k0 = 0; k0 < K; k0 += KG) {
+    const int kn = K - k0 < KG ? K - k0 : KG;
+    int pk[KG];
+    float sk[KG], part[KG];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        part += fd[q] * fy[q];
-        o[q] = s * fd[q];
-      }
-      dyr[c] = pack8(o);
+    for (int j = 0; j < KG; ++j) {
+      pk[j] = j < kn ? pos[(int64_t)t * K + k0 + j] : -1;
+      sk[j] = j < kn ? scores[(int64_t)t * K + k0 + j] : 0.0f;
+      part[j] = 0.0f;
     }
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-    if (lane == 0) dscores[(int64_t)t * K + k] = part;
+    for (int c = lane; c < nch; c += 64) {
+      float fd[8];
+      unpack8(dr[c], fd);
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        if (pk[j] < 0) continue;  // wave-uniform
+        float fy[8], o[8];
+        unpack8(y[(int64_t)pk[j] * nch + c], fy);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          part[j] += fd[q] * fy[q];
+          o[q] = sk[j] * fd[q];
+        }
+        dy[(int64_t)pk[j] * nch + c] = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      if (j >= kn) break;
+      float v = part[j];
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) dscores[(int64_t)t * K + k0 + j] = pk[j] < 0 ? 0.0f : v;
+    }
   }
 }
 
