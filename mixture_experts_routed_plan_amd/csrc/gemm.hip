@@ -37,6 +37,8 @@
 //     places on one XCD (workgroup id mod 8) take 32 consecutive logical tiles, and logical tiles
 //     run 8 row tiles deep before the next column tiles, so concurrently running tiles of an XCD
 //     share operand panels in that XCD's L2.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -148,13 +150,21 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
 // LDS-DMA it knows about makes it wait for every outstanding LDS read); the copies are waited for
 // explicitly (s_waitcnt 0) before each barrier. M0 carries the LDS address; the kernels that use
 // this have no other use of M0.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, const uint16_t* lds) {
-  typedef __attribute__((address_space(3))) const uint16_t* lds_ptr;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(off), "s"(base), "s"(m0)
                : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array. Taken once per kernel, of the array
+// itself, and offset with integer arithmetic from there: the compiler folds the cast of the
+// array's address to a constant, where a cast of a computed generic pointer would carry a null
+// test.
+__device__ __forceinline__ uint32_t lds_address(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) const uint16_t* lds_ptr;
+  return (uint32_t)(uintptr_t)(lds_ptr)p;
 }
 
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
@@ -187,9 +197,10 @@ struct DmaTile {
       off[i] = row_off(row) + swz<kBK>(row, lane & 7) * 16;
     }
   }
-  __device__ __forceinline__ void issue(const uint16_t* lds_tile, int k0, int i) const {
+  // lds_tile: LDS byte address of the tile
+  __device__ __forceinline__ void issue(uint32_t lds_tile, int k0, int i) const {
     const int blk = (threadIdx.x >> 6) * NB + i;
-    dma16(base + (int64_t)k0 * 2, off[i], lds_tile + blk * 8 * kBK);
+    dma16(base + (int64_t)k0 * 2, off[i], lds_tile + blk * 8 * kBK * 2);
   }
 };
 
@@ -227,11 +238,11 @@ struct MnTile {
   }
   // copy k rows [k0, k0+64) of the tile (k counted from kbeg); rows at or past klim (relative
   // count of valid rows) are clamped to klim - 1
-  __device__ __forceinline__ void issue(const uint16_t* lds_tile, int k0, int klim, int i) const {
+  __device__ __forceinline__ void issue(uint32_t lds_tile, int k0, int klim, int i) const {
     const int blk = (threadIdx.x >> 6) * NB + i;
     int k = k0 + row[i];
     if (k > klim - 1) k = klim - 1;  // k0 <= klim - 1 whenever the stage exists
-    dma16(base + (int64_t)k0 * ldb, (uint32_t)((k - k0) * ldb) + col[i], lds_tile + blk * 2 * R);
+    dma16(base + (int64_t)k0 * ldb, (uint32_t)((k - k0) * ldb) + col[i], lds_tile + blk * 2 * R * 2);
   }
 };
 
@@ -266,7 +277,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   Tile t;
   if (!decode_tile<BM, BN, SCHED, EPI>(g, t)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches
   const int wr = wave & 1, wc = wave >> 1;
   const int klen = t.kend - t.kbeg;
 
@@ -322,15 +334,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int nk = (klen + BK - 1) / BK;
   auto bufP = [&](int b) { return lds + b * (BM + BN) * BK; };
   auto bufQ = [&](int b) { return lds + b * (BM + BN) * BK + BM * BK; };
+  const uint32_t lds0 = lds_address(lds);  // byte addresses of the stage buffers for the copies
+  auto addrP = [&](int b) { return lds0 + (uint32_t)(b * (BM + BN) * BK * 2); };
+  auto addrQ = [&](int b) { return lds0 + (uint32_t)((b * (BM + BN) * BK + BM * BK) * 2); };
 
   // copy of one stage: 8 DMA blocks per operand and wavefront
   static_assert(DmaTile<BM>::NB == 8 && MnTile<BM>::NB == 8, "8 copies per operand");
   auto copy_issue = [&](int b, int kt, int n) {
     const int k0 = kt * BK;  // relative to kbeg
     if (n < 8) {
-      if constexpr (P_KC) pd.issue(bufP(b), t.kbeg + k0, n); else pm.issue(bufP(b), k0, klen, n);
+      if constexpr (P_KC) pd.issue(addrP(b), t.kbeg + k0, n); else pm.issue(addrP(b), k0, klen, n);
     } else {
-      if constexpr (Q_KC) qd.issue(bufQ(b), t.kbeg + k0, n - 8); else qm.issue(bufQ(b), k0, klen, n - 8);
+      if constexpr (Q_KC) qd.issue(addrQ(b), t.kbeg + k0, n - 8); else qm.issue(addrQ(b), k0, klen, n - 8);
     }
   };
 
@@ -387,6 +402,56 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   //                        stage have landed, and this buffer is no longer read after this point
   //   ks = 3, m >= 12:     the read operations of sub-step 0 of the next stage
   // The buffer written during stage s was last read before the barrier of stage s-1.
+  // this wavefront's 32-row blocks (jlim of FM) and 32-column blocks (ilim of FN; for the SwiGLU
+  // forward per gate/up half) that hold any output: the products of the others (the ragged last
+  // row tile of an expert, a column tail) are skipped
+  const int rows_left = t.r_lim - (t.r0 + wr * WM);
+  const int jlim = rows_left <= 0 ? 0 : (rows_left >= WM ? FM : (rows_left + 31) / 32);
+  int ilim;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    const int cols_left = g.F - (t.n0 + wc * (WN / 2));
+    ilim = cols_left <= 0 ? 0 : (cols_left >= WN / 2 ? FN / 2 : (cols_left + 31) / 32);
+  } else {
+    const int cols_left = g.N_out - (t.n0 + wc * WN);
+    ilim = cols_left <= 0 ? 0 : (cols_left >= WN ? FN : (cols_left + 31) / 32);
+  }
+  auto block_on = [&](int i, int j) {
+    return (EPI == EPI_SWIGLU_FWD ? (i % (FN / 2)) < ilim : i < ilim) && j < jlim;
+  };
+  // one k stage; MASKED: skip the products of empty blocks (a tile with a ragged edge; full tiles
+  // run the unmasked copy of the body)
+  auto stage = [&](int kt, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const bool more = kt + 1 < nk;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      mask_tail(kt, ks);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if (ks == 3 && m == 12) {
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!MASKED || block_on(m >> 2, m & 3))
+          acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              qa[ks & 1][m >> 2], pb[ks & 1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+        if (ks < 3) {
+#pragma unroll
+          for (int n = (m * NR) / 16; n < ((m + 1) * NR) / 16; ++n) read_op(cur, ks + 1, n);
+        }
+        if (more) {
+          if (ks < 2 && (m & 1) == 1) copy_issue(nxt, kt + 1, ks * 8 + (m >> 1));
+          if (ks == 3 && m >= 12) {
+#pragma unroll
+            for (int n = ((m - 12) * NR) / 4; n < ((m - 11) * NR) / 4; ++n) read_op(nxt, 0, n);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   if (nk > 0) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) copy_issue(0, 0, n);
@@ -394,35 +459,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < NR; ++n) read_op(0, 0, n);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1, nxt = cur ^ 1;
-      const bool more = kt + 1 < nk;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        mask_tail(kt, ks);
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          if (ks == 3 && m == 12) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              qa[ks & 1][m >> 2], pb[ks & 1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
-          if (ks < 3) {
-#pragma unroll
-            for (int n = (m * NR) / 16; n < ((m + 1) * NR) / 16; ++n) read_op(cur, ks + 1, n);
-          }
-          if (more) {
-            if (ks < 2 && (m & 1) == 1) copy_issue(nxt, kt + 1, ks * 8 + (m >> 1));
-            if (ks == 3 && m >= 12) {
-#pragma unroll
-              for (int n = ((m - 12) * NR) / 4; n < ((m - 11) * NR) / 4; ++n) read_op(nxt, 0, n);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    if (jlim == FM && ilim == (EPI == EPI_SWIGLU_FWD ? FN / 2 : FN)) {
+      for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{});
+    } else {
+      for (int kt = 0; kt < nk; ++kt) stage(kt, std::true_type{});
     }
   }
 
@@ -463,6 +503,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     constexpr int PW = WN + 4;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
+      if (j >= jlim) break;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -481,6 +522,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int f0w = t.n0 + wc * W;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
+      if (j >= jlim) break;
 #pragma unroll
       for (int i = 0; i < FN / 2; ++i)
 #pragma unroll
@@ -512,6 +554,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     constexpr int per_row = WN / 8, rows_per_pass = 64 / per_row;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
+      if (j >= jlim) break;
       const int row0 = t.r0 + wr * WM + j * 32;
       // coalesced loads of the g and u row segments (rows past the segment clamped)
 #pragma unroll
