@@ -72,6 +72,9 @@ def lib():
             L.oracle_tokens.argtypes = [S, P, P, P, P, P, P, I64, P, P, P, P, P]
             L.oracle_wgrad_entries.restype = ctypes.c_int
             L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P]
+            L.oracle_route.restype = ctypes.c_int
+            L.oracle_route.argtypes = [I64, I64, I64, P, ctypes.c_int32, ctypes.c_int32, I64, I64,
+                                       P, P]
             _lib = L
     return _lib
 
@@ -199,3 +202,21 @@ def wgrad_entries(x, ids, scores, w13, w2, dout, e: int, jd: np.ndarray, df: np.
     lib().oracle_wgrad_entries(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2),
                                _p(dout), int(e), len(jd), _p(jd), _p(v13), len(df), _p(df), _p(v2))
     return v13, v2
+
+
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+
+
+def route(logits: np.ndarray, K: int, score_fn: int = SCORE_SOFTMAX, renormalize: bool = True,
+          n_group: int = 1, topk_group: int = 1):
+    """Router: expert ids [T,K] (int64, selection order) and weights [T,K] (float64) from fp32
+    logits [T,E]; see the router section of moe_oracle.c for the definition."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.zeros((T, K), np.int64)
+    w = np.zeros((T, K), np.float64)
+    rc = lib().oracle_route(T, E, K, _p(logits), int(score_fn), 1 if renormalize else 0,
+                            int(n_group), int(topk_group if n_group > 1 else 1), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("bad router configuration")
+    return ids, w

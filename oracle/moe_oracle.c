@@ -455,3 +455,101 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
   free(fl);
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------- */
+/* router: score function and (group-limited) top-k                                             */
+/*
+ * MegaMoE (ROCm Primus technical guide), introduction: the expert path is preceded by a router made
+ * of a score function and a group-limited top-k. Primus, "Router force load balancing", `uniform`:
+ * the router then works on random logits. The pages name the pieces but give no formulas; the
+ * readings taken here:
+ *   - scores: softmax over the E logits of a token, or the elementwise logistic sigmoid;
+ *   - both are strictly increasing in a token's own logit, so the experts with the largest scores
+ *     are the experts with the largest logits: selection compares logits (ties: lower index
+ *     first; NaN counts as below every number);
+ *   - group-limited: the E experts form n_group equal groups of consecutive ids; a group's score is
+ *     its largest logit; the topk_group best groups are kept (ties: lower group first) and the K
+ *     experts are chosen among the kept groups' experts only;
+ *   - weights: renormalize = 0 gives the chosen experts' scores as computed over all E experts
+ *     (softmax) or per expert (sigmoid); renormalize = 1 divides them by their sum over the K
+ *     chosen, which for softmax equals the softmax of the K chosen logits;
+ *   - ids are written in selection order (descending logit).
+ */
+#define ORACLE_SCORE_SOFTMAX 0
+#define ORACLE_SCORE_SIGMOID 1
+
+/* a ranks before b: larger value, or equal value and lower index; NaN below every number */
+static int ranks_before(double va, int64_t ia, double vb, int64_t ib) {
+  const int na = isnan(va), nb = isnan(vb);
+  if (na != nb) return nb;
+  if (!na && va != vb) return va > vb;
+  return ia < ib;
+}
+
+int oracle_route(int64_t T, int64_t E, int64_t K, const float* logits, int32_t score_fn,
+                 int32_t renormalize, int64_t n_group, int64_t topk_group, int64_t* ids,
+                 double* weights) {
+  if (E < 1 || K < 1 || K > E || n_group < 1 || E % n_group != 0 || topk_group < 1 ||
+      topk_group > n_group || K > topk_group * (E / n_group))
+    return -1;
+  const int64_t gs = E / n_group;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    char* allowed = (char*)calloc((size_t)E, 1);
+    char* taken = (char*)calloc((size_t)E, 1);
+    char* gtaken = (char*)calloc((size_t)n_group, 1);
+    /* groups */
+    for (int64_t r = 0; r < topk_group; ++r) {
+      int64_t best = -1;
+      double bestv = 0.0;
+      for (int64_t g = 0; g < n_group; ++g) {
+        if (gtaken[g]) continue;
+        int64_t gi = g * gs;  /* the group's best expert, compared like experts */
+        for (int64_t e = g * gs + 1; e < (g + 1) * gs; ++e)
+          if (ranks_before((double)l[e], e, (double)l[gi], gi)) gi = e;
+        if (best < 0 || ranks_before((double)l[gi], g, bestv, best)) {
+          best = g;
+          bestv = (double)l[gi];
+        }
+      }
+      gtaken[best] = 1;
+      for (int64_t e = best * gs; e < (best + 1) * gs; ++e) allowed[e] = 1;
+    }
+    /* experts */
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < E; ++e) {
+        if (!allowed[e] || taken[e]) continue;
+        if (best < 0 || ranks_before((double)l[e], e, (double)l[best], best)) best = e;
+      }
+      taken[best] = 1;
+      ids[t * K + k] = best;
+    }
+    /* weights */
+    double* w = weights + t * K;
+    if (score_fn == ORACLE_SCORE_SOFTMAX) {
+      double m = -INFINITY, z = 0.0;
+      if (renormalize) {
+        for (int64_t k = 0; k < K; ++k) m = fmax(m, (double)l[ids[t * K + k]]);
+        for (int64_t k = 0; k < K; ++k) z += exp((double)l[ids[t * K + k]] - m);
+      } else {
+        for (int64_t e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+        for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - m);
+      }
+      for (int64_t k = 0; k < K; ++k) w[k] = exp((double)l[ids[t * K + k]] - m) / z;
+    } else {
+      double z = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        w[k] = 1.0 / (1.0 + exp(-(double)l[ids[t * K + k]]));
+        z += w[k];
+      }
+      if (renormalize)
+        for (int64_t k = 0; k < K; ++k) w[k] /= z;
+    }
+    free(allowed);
+    free(taken);
+    free(gtaken);
+  }
+  return 0;
+}
