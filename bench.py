@@ -275,11 +275,25 @@ def main():
     from mixture_experts_routed_plan_amd import moe_trace
 
     w = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+
+    def gpu_router(logits, K):
+        # logit-routed workloads: the layer's own router on the GPU (softmax top-K, renormalised)
+        import mixture_experts_routed_plan_amd as M
+        T, E = logits.shape
+        lg = torch.from_numpy(logits).cuda()
+        ids_d = torch.empty((T, K), dtype=torch.int64, device="cuda")
+        sc_d = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        shape = M.make_shape(T, 64, 64, E, K, ids_dtype=M.MOE_IDS_I64)
+        M.check(M.moe_route(shape, M.make_router(), lg, ids_d, sc_d), "moe_route")
+        torch.cuda.synchronize()
+        return ids_d.cpu().numpy(), sc_d.cpu().numpy()
+
     t0 = time.time()
-    inp = W.make_inputs(w, with_dout=True)
+    inp = W.make_inputs(w, with_dout=True,
+                        router=gpu_router if w.routing in W.LOGIT_ROUTINGS else None)
     log("bench: %s inputs drawn in %.1fs" % (w.name, time.time() - t0))
 
-    torch.cuda.set_device(0)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src_buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")

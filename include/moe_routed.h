@@ -174,6 +174,36 @@ moe_status moe_plan_status(const moe_shape* shape, const void* plan, int64_t* ba
 moe_status moe_saved_views(const moe_shape* shape, void* saved, uint16_t** xg, uint16_t** h13,
                            uint16_t** a, uint16_t** y);
 
+/* Router (MegaMoE, ROCm Primus guide, introduction: score function + group-limited top-k ahead
+ * of the expert path; Primus "Router force load balancing", uniform: routing of random logits).
+ * From logits[T,E] fp32 it writes topk_ids[T,K] (shape.ids_dtype) and scores[T,K] fp32, ready for
+ * moe_plan / moe_forward:
+ *   score: MOE_SCORE_SOFTMAX (softmax over the token's E logits) or MOE_SCORE_SIGMOID (logistic
+ *          sigmoid of each logit). Both increase with the logit, so the chosen experts are the K
+ *          largest logits, in descending order (ties: lower expert id first; NaN ranks last).
+ *   group limit: n_group > 1 splits the experts into n_group groups of E/n_group consecutive ids;
+ *          a group ranks by its largest logit (ties: lower group), and only the experts of the
+ *          topk_group best groups can be chosen. n_group <= 1 means no group limit.
+ *   weights: the chosen experts' scores; with renormalize != 0 divided by their sum over the K
+ *          chosen (for softmax: the softmax of the K chosen logits). fp32, expf.
+ * Reads shape.T, E, K and ids_dtype only (1 <= E <= MOE_MAX_EXPERTS, 1 <= K <= min(E,
+ * MOE_MAX_TOPK)); requires n_group <= 64 dividing E, 1 <= topk_group <= n_group and
+ * K <= topk_group * E / n_group. logits and scores 4-byte aligned, topk_ids aligned to its type.
+ * Errors as for the other calls; nothing is enqueued on a host-side error. */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+#define MOE_MAX_GROUPS 64
+
+typedef struct moe_router {
+  int32_t score_fn;    /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID */
+  int32_t renormalize; /* != 0: weights divided by their sum over the K chosen experts */
+  int32_t n_group;     /* expert groups; <= 1: no group limit */
+  int32_t topk_group;  /* groups kept per token when n_group > 1 */
+} moe_router;
+
+moe_status moe_route(const moe_shape* shape, const moe_router* router, const float* logits,
+                     void* topk_ids, float* scores, hipStream_t stream, const moe_trace* trace);
+
 const char* moe_status_str(int status);
 int moe_abi_version(void);
 

@@ -20,6 +20,9 @@ MOE_SAVE_FOR_BACKWARD = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_TRACE_MAX_EVENTS = 8
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
+MOE_MAX_GROUPS = 64
 
 MOE_OK = 0
 MOE_E_NULL = -1
@@ -46,6 +49,11 @@ class moe_trace(ctypes.Structure):
                 ("events", ctypes.c_void_p * MOE_TRACE_MAX_EVENTS)]
 
 
+class moe_router(ctypes.Structure):
+    _fields_ = [("score_fn", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -70,6 +78,7 @@ def _load():
         "moe_plan_status": (St, [S, P, ctypes.POINTER(ctypes.c_int64), P]),
         "moe_saved_views": (St, [S, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
                                  ctypes.POINTER(P)]),
+        "moe_route": (St, [S, ctypes.POINTER(moe_router), P, P, P, P, Tr]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_abi_version": (ctypes.c_int, []),
     }
@@ -83,7 +92,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_plan_bytes", "moe_saved_bytes", "moe_workspace_bytes", "moe_plan", "moe_forward",
             "moe_backward", "moe_plan_export", "moe_plan_status", "moe_saved_views",
-            "moe_status_str", "moe_abi_version")
+            "moe_route", "moe_status_str", "moe_abi_version")
 
 
 def _ptr(t):
@@ -151,6 +160,16 @@ def moe_backward(shape, plan, saved, dout, scores, w13, w2, dx, dw13, dw2, dscor
                              _ptr(scores), _ptr(w13), _ptr(w2), _ptr(dx), _ptr(dw13), _ptr(dw2),
                              _ptr(dscores), _ptr(workspace), _stream(stream),
                              None if trace is None else ctypes.byref(trace))
+
+
+def make_router(score_fn=MOE_SCORE_SOFTMAX, renormalize=True, n_group=1, topk_group=1) -> moe_router:
+    return moe_router(int(score_fn), 1 if renormalize else 0, int(n_group), int(topk_group))
+
+
+def moe_route(shape, router, logits, topk_ids, scores, stream=None, trace=None) -> int:
+    return _lib.moe_route(ctypes.byref(shape), ctypes.byref(router), _ptr(logits), _ptr(topk_ids),
+                          _ptr(scores), _stream(stream),
+                          None if trace is None else ctypes.byref(trace))
 
 
 def moe_plan_export(shape, plan, counts=None, offsets=None, pos=None, src=None,

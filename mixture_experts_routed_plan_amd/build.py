@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_routed.so")
-SOURCES = ["abi.hip", "plan.hip", "rowops.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "plan.hip", "rowops.hip", "gemm.hip", "router.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed-fp32 instruction forms are switched off for all device code

@@ -183,6 +183,30 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   return MOE_OK;
 }
 
+moe_status moe_route(const moe_shape* s, const moe_router* r, const float* logits,
+                     void* topk_ids, float* scores, hipStream_t stream, const moe_trace* trace) {
+  if (!s || !r) return MOE_E_NULL;
+  if (s->ids_dtype != MOE_IDS_I32 && s->ids_dtype != MOE_IDS_I64) return MOE_E_DTYPE;
+  if (r->score_fn != MOE_SCORE_SOFTMAX && r->score_fn != MOE_SCORE_SIGMOID) return MOE_E_DTYPE;
+  if (s->T < 1 || s->E < 1 || s->E > MOE_MAX_EXPERTS || s->K < 1 || s->K > MOE_MAX_TOPK ||
+      s->K > s->E || s->T > (int64_t)(INT32_MAX - 1) / s->K)
+    return MOE_E_SHAPE;
+  if (r->n_group > 1) {
+    if (r->n_group > MOE_MAX_GROUPS || s->E % r->n_group != 0 || r->topk_group < 1 ||
+        r->topk_group > r->n_group || s->K > (int64_t)r->topk_group * (s->E / r->n_group))
+      return MOE_E_SHAPE;
+  }
+  if (!logits || !topk_ids || !scores) return MOE_E_NULL;
+  if (!aligned(logits, 4) || !aligned(scores, 4) ||
+      !aligned(topk_ids, s->ids_dtype == MOE_IDS_I64 ? 8 : 4))
+    return MOE_E_ALIGN;
+  Tracer tr{trace, stream, 0};
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_route(*s, *r, logits, topk_ids, scores, stream));
+  MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
 moe_status moe_plan_export(const moe_shape* s, const void* plan, int32_t* counts,
                            int32_t* offsets, int32_t* pos, int32_t* src, hipStream_t stream) {
   moe_status st = check_shape(s);

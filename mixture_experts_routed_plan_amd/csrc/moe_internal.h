@@ -161,6 +161,10 @@ hipError_t launch_combine_bwd(const moe_shape& s, const int32_t* pos, const uint
                               const uint16_t* y, const float* scores, uint16_t* dy,
                               float* dscores, hipStream_t st);
 
+// router: logits[T,E] -> ids[T,K] (shape.ids_dtype), weights[T,K]; arguments validated by the caller
+hipError_t launch_route(const moe_shape& s, const moe_router& r, const float* logits, void* ids,
+                        float* weights, hipStream_t st);
+
 // grouped GEMMs
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
                             const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st);

@@ -107,6 +107,27 @@ def test_null_and_alignment_rejected():
     assert M.moe_plan_status(s, None, 0)[0] == M.MOE_E_NULL
 
 
+def test_router_arguments_rejected():
+    a = 4096
+    s = shape(E=16, K=4)
+    r = M.make_router()
+    assert M.moe_route(s, r, None, a, a, 0) == M.MOE_E_NULL
+    assert M.moe_route(s, r, a + 2, a, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_route(s, r, a, a + 4, a, 0) == M.MOE_E_ALIGN  # int64 ids
+    assert M.moe_route(s, r, a, a, a + 1, 0) == M.MOE_E_ALIGN
+    assert M.moe_route(s, M.make_router(score_fn=5), a, a, a, 0) == M.MOE_E_DTYPE
+    for kw in [dict(K=17), dict(E=1025, K=4), dict(K=65, E=128), dict(T=0)]:
+        assert M.moe_route(shape(**dict(dict(E=16, K=4), **kw)), r, a, a, a, 0) == M.MOE_E_SHAPE
+    # (only invalid configurations here: a valid one would launch on the bogus addresses)
+    for rk in [dict(n_group=3, topk_group=1), dict(n_group=4, topk_group=0),
+               dict(n_group=4, topk_group=5), dict(n_group=8, topk_group=1),
+               dict(n_group=128, topk_group=2)]:
+        assert M.moe_route(s, M.make_router(**rk), a, a, a, 0) == M.MOE_E_SHAPE, rk
+    # the router does not read D, F or flags
+    s3 = shape(E=16, K=4, D=100)
+    assert M.moe_route(s3, r, None, a, a, 0) == M.MOE_E_NULL
+
+
 def test_importing_without_the_library_fails_loudly(tmp_path):
     code = ("import sys, os; sys.path.insert(0, %r); import mixture_experts_routed_plan_amd as M"
             % str(tmp_path))

@@ -114,7 +114,7 @@ PLAN_CASES = list(W.WORKLOADS) + list(W.PARITY_WORKLOADS)
 def test_plan_bit_exact(name, ids_dtype):
     M, dv = _lib()
     w = {**W.WORKLOADS, **W.PARITY_WORKLOADS}[name]
-    ids, _ = W.routing(w, ids_dtype)
+    ids, _ = W.routing(w, ids_dtype, router=oracle.route)
     layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, ids_dtype=ids_dtype, save_for_backward=False,
                      alloc_grads=False)
     layer.plan(torch.from_numpy(ids).cuda())
@@ -177,7 +177,7 @@ def _full_check(inp, layer):
 @pytest.mark.parametrize("name", FULL_CASES)
 def test_layer_parity_every_element(name):
     w = {**W.WORKLOADS, **W.PARITY_WORKLOADS}[name]
-    inp = W.make_inputs(w)
+    inp = W.make_inputs(w, router=oracle.route)
     log("\n[%s] T=%d D=%d F=%d E=%d K=%d" % (name, w.T, w.D, w.F, w.E, w.K))
     layer, _ = run(inp)
     _full_check(inp, layer)
@@ -185,7 +185,7 @@ def test_layer_parity_every_element(name):
 
 def test_layer_parity_int32_ids_and_bad_ids():
     w = W.PARITY_WORKLOADS["p_ragged"].with_(T=333)
-    inp = W.make_inputs(w, ids_dtype=np.int32)
+    inp = W.make_inputs(w, ids_dtype=np.int32, router=oracle.route)
     inp.ids[5, 1] = w.E + 3
     inp.ids[77, 0] = -1
     layer, _ = run(inp, ids_dtype=np.int32)
@@ -196,7 +196,7 @@ def test_layer_parity_int32_ids_and_bad_ids():
 
 def test_forward_without_save_matches_saving_forward():
     _, dv = _lib()
-    inp = W.make_inputs(W.PARITY_WORKLOADS["p_ragged"])
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_ragged"], router=oracle.route)
     l1, _ = run(inp, backward=False, save=True)
     l2, _ = run(inp, backward=False, save=False)
     np.testing.assert_array_equal(dv.to_host_bits(l1.out), dv.to_host_bits(l2.out))
@@ -204,7 +204,7 @@ def test_forward_without_save_matches_saving_forward():
 
 def test_repeated_calls_are_bitwise_identical():
     _, dv = _lib()
-    inp = W.make_inputs(W.PARITY_WORKLOADS["p_skew"])
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_skew"], router=oracle.route)
     l1, d = run(inp)
     outs = [dv.to_host_bits(t) for t in (l1.out, l1.dx, l1.dw13, l1.dw2)] + [
         l1.dscores.cpu().numpy()]
@@ -231,7 +231,7 @@ def _large(name):
     _, dv = _lib()
     w = W.WORKLOADS[name]
     t0 = time.time()
-    inp = W.make_inputs(w, with_dout=True)
+    inp = W.make_inputs(w, with_dout=True, router=oracle.route)
     log("\n[%s] inputs drawn in %.1fs" % (name, time.time() - t0))
     layer, d = run(inp, backward=True, save=True)
     log("[%s] gpu forward+backward done" % name)

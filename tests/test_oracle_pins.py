@@ -158,7 +158,7 @@ def test_plan_matches_stable_argsort(seed):
 def test_plan_conservation_on_workloads():
     for name in ("fine_grained", "imbalanced", "training"):
         w = W.WORKLOADS[name]
-        ids, _ = W.routing(w)
+        ids, _ = W.routing(w, router=oracle.route)
         pl = oracle.plan(ids, w.E)
         assert pl["counts"].sum() == w.T * w.K and pl["bad"] == 0
     c = oracle.plan(W.routing(W.WORKLOADS["imbalanced"])[0], 32)["counts"]
@@ -266,7 +266,7 @@ def test_bf16_mode_matches_dense_bf16_brute_force(kw):
 
 
 def test_bf16_mode_close_to_exact_evaluation():
-    inp = W.make_inputs(W.PARITY_WORKLOADS["p_wide"].with_(T=64))
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_wide"].with_(T=64), router=oracle.route)
     b = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16")
     e = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="exact")
     for k in ("out", "dx", "dw13", "dw2", "dscores"):

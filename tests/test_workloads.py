@@ -1,7 +1,11 @@
 """The seeded input generators: determinism, shapes and the routing rules' stated properties."""
 import numpy as np
+import pytest
 
+import oracle
 import workloads as W
+
+ROUTER = oracle.route  # (logits, K) -> (ids, weights): softmax top-K, renormalised
 
 
 def test_inputs_deterministic_and_shaped():
@@ -27,7 +31,7 @@ def test_block_streams_do_not_depend_on_thread_count(monkeypatch):
 
 
 def test_weight_scale_is_inverse_sqrt_fan_in():
-    inp = W.make_inputs(W.PARITY_WORKLOADS["p_wide"])
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_wide"], router=ROUTER)
     w = inp.w
     assert abs(W.bf16_bits_to_f32(inp.w13).std() * np.sqrt(w.D) - 1) < 0.02
     assert abs(W.bf16_bits_to_f32(inp.w2).std() * np.sqrt(w.F) - 1) < 0.02
@@ -41,10 +45,14 @@ def test_routing_rules():
     k = np.arange(w.K)[None, :]
     np.testing.assert_array_equal(ids, (t * w.K + k) % w.E)
     assert (s == 0.5).all()
-    # top-k of softmax: ids distinct, scores renormalised and descending
+    # top-k of softmax (routed by the oracle's router): ids distinct, scores renormalised and
+    # descending; without a router the generator refuses
     for name in ("fine_grained", "training"):
         w = W.WORKLOADS[name]
-        ids, s = W.routing(w)
+        with pytest.raises(ValueError):
+            W.routing(w)
+        ids, s = W.routing(w, router=ROUTER)
+        assert W.router_logits(w).shape == (w.T, w.E)
         assert ids.shape == (w.T, w.K)
         srt = np.sort(ids, 1)
         assert (srt[:, 1:] != srt[:, :-1]).all()

@@ -13,7 +13,9 @@ Recipe (every config):
 * Dense tensors: float32 standard normal, scaled by ``std`` in float32, then rounded to bf16
   (round-to-nearest-even). ``x`` and ``dout`` use std 1; ``w13`` uses 1/sqrt(D) and ``w2`` uses
   1/sqrt(F) (std = 1/sqrt(fan_in), fan_in being the contracted width).
-* Routing follows the workload's rule (see ``ROUTINGS``); scores are float32.
+* Routing follows the workload's rule (see ``ROUTINGS``); scores are float32. Logit-routed
+  workloads (``LOGIT_ROUTINGS``) draw only the router logits here (``router_logits``); their ids
+  and scores come from a router the caller passes in (the GPU router, or the oracle's in tests).
 
 The workloads are the five shapes the pages' systems run at one GPU's share (Dist-MoE quickstart
 shape; a fine-grained 64-expert shard; a 7168-hidden expert-parallel shard, balanced and at
@@ -165,13 +167,9 @@ def _route_even(w: Workload, rng):
     return ids, scores
 
 
-def _route_topk_softmax(w: Workload, rng):
-    # router logits ~ N(0,1); ids = top-K in descending logit order (ties -> lower index);
-    # scores = softmax over the K chosen logits (renormalised)
-    logits = rng.standard_normal((w.T, w.E), dtype=np.float32)
-    order = np.argsort(-logits, axis=1, kind="stable")[:, : w.K]
-    chosen = np.take_along_axis(logits, order, axis=1)
-    return order.astype(np.int64), _softmax_rows(chosen)
+def _logits(w: Workload, rng):
+    # router logits ~ N(0,1) (Primus "uniform" forced balancing: random logits, then routing)
+    return rng.standard_normal((w.T, w.E), dtype=np.float32)
 
 
 def _route_uniform_distinct(w: Workload, rng):
@@ -242,16 +240,37 @@ def _route_skewed(w: Workload, rng):
 
 ROUTINGS = {
     "even": _route_even,
-    "topk_softmax": _route_topk_softmax,
     "uniform_distinct": _route_uniform_distinct,
     "zipf_peak3": _route_zipf_peak3,
     "skewed": _route_skewed,
 }
 
 
-def routing(w: Workload, ids_dtype=np.int64):
+# routing rules that start from router logits: the ids and scores come from a router (softmax
+# top-K, renormalised over the K chosen) that the caller supplies
+LOGIT_ROUTINGS = ("topk_softmax",)
+
+
+def router_logits(w: Workload) -> np.ndarray:
+    """fp32 router logits [T,E] of a logit-routed workload."""
+    if w.routing not in LOGIT_ROUTINGS:
+        raise ValueError("workload %s is not routed from logits" % w.name)
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, TAG_ROUTE])))
-    ids, scores = ROUTINGS[w.routing](w, rng)
+    return np.ascontiguousarray(_logits(w, rng))
+
+
+def routing(w: Workload, ids_dtype=np.int64, router=None):
+    """(ids [T,K], scores [T,K] fp32). For logit-routed workloads ``router(logits, K)`` must be
+    given and returns (ids, weights) of the softmax top-K router, renormalised over the K chosen."""
+    if w.routing in LOGIT_ROUTINGS:
+        if router is None:
+            raise ValueError("workload %s is routed from logits: pass a router" % w.name)
+        ids, scores = router(router_logits(w), w.K)
+    else:
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, TAG_ROUTE])))
+        ids, scores = ROUTINGS[w.routing](w, rng)
+    ids = np.asarray(ids)
+    scores = np.asarray(scores)
     return np.ascontiguousarray(ids.astype(ids_dtype)), np.ascontiguousarray(scores, dtype=np.float32)
 
 
@@ -266,14 +285,16 @@ class Inputs:
     dout: np.ndarray | None  # [T,D] uint16 or None
 
 
-def make_inputs(w: Workload, ids_dtype=np.int64, with_dout: bool | None = None) -> Inputs:
-    """Draw every input of workload ``w`` (deterministic in ``w.seed``)."""
+def make_inputs(w: Workload, ids_dtype=np.int64, with_dout: bool | None = None,
+                router=None) -> Inputs:
+    """Draw every input of workload ``w`` (deterministic in ``w.seed``); ``router`` as in
+    ``routing`` for logit-routed workloads."""
     if with_dout is None:
         with_dout = w.backward
     x = normal_bf16(w.seed, TAG_X, (w.T, w.D), 1.0)
     w13 = normal_bf16(w.seed, TAG_W13, (w.E, 2, w.F, w.D), 1.0 / math.sqrt(w.D))
     w2 = normal_bf16(w.seed, TAG_W2, (w.E, w.D, w.F), 1.0 / math.sqrt(w.F))
-    ids, scores = routing(w, ids_dtype)
+    ids, scores = routing(w, ids_dtype, router)
     dout = normal_bf16(w.seed, TAG_DOUT, (w.T, w.D), 1.0) if with_dout else None
     return Inputs(w, x, w13, w2, ids, scores, dout)
 
