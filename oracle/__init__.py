@@ -33,7 +33,7 @@ IN_BF16, IN_F64 = 0, 1
 class _Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
                 ("E", ctypes.c_int64), ("K", ctypes.c_int64), ("round_bf16", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("wgrad_f32", ctypes.c_int32)]
 
 
 def build(force: bool = True) -> str:
@@ -67,11 +67,11 @@ def lib():
             L.oracle_forward.restype = ctypes.c_int
             L.oracle_forward.argtypes = [S] + [P] * 12
             L.oracle_backward.restype = ctypes.c_int
-            L.oracle_backward.argtypes = [S] + [P] * 19
+            L.oracle_backward.argtypes = [S] + [P] * 21
             L.oracle_tokens.restype = ctypes.c_int
             L.oracle_tokens.argtypes = [S, P, P, P, P, P, P, I64, P, P, P, P, P]
             L.oracle_wgrad_entries.restype = ctypes.c_int
-            L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P]
+            L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P, P, P]
             L.oracle_route.restype = ctypes.c_int
             L.oracle_route.argtypes = [I64, I64, I64, P, ctypes.c_int32, ctypes.c_int32, I64, I64,
                                        P, P]
@@ -83,10 +83,10 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _shape(T, D, F, E, K, mode, in_dtype):
+def _shape(T, D, F, E, K, mode, in_dtype, wgrad_f32=False):
     if mode not in ("bf16", "exact"):
         raise ValueError(mode)
-    return _Shape(T, D, F, E, K, 1 if mode == "bf16" else 0, in_dtype)
+    return _Shape(T, D, F, E, K, 1 if mode == "bf16" else 0, in_dtype, 1 if wgrad_f32 else 0)
 
 
 def _as_input(a, in_dtype):
@@ -124,11 +124,14 @@ def plan(ids: np.ndarray, E: int) -> dict:
     return dict(counts=counts, offsets=offsets, pos=pos, src=src, bad=int(bad))
 
 
-def full(x, ids, scores, w13, w2, dout=None, mode: str = "bf16") -> dict:
+def full(x, ids, scores, w13, w2, dout=None, mode: str = "bf16", wgrad_f32: bool = False,
+         dw13_init=None, dw2_init=None) -> dict:
     """Whole layer on small shapes: plan, forward, and backward when dout is given.
 
     Returns every intermediate: xg, h13, a, y, out (+ dy, dscores, dh13, dxg, dx, dw13, dw2),
-    all float64, plus the plan arrays."""
+    all float64, plus the plan arrays. wgrad_f32: the weight gradients are stored in fp32 (not
+    rounded to bf16); dw13_init / dw2_init: existing gradients that the new ones accumulate into
+    (values, e.g. bf16 bit patterns widened, or float32)."""
     T, D = x.shape
     E, two, F, D2 = w13.shape
     assert two == 2 and D2 == D and w2.shape == (E, D, F)
@@ -137,8 +140,10 @@ def full(x, ids, scores, w13, w2, dout=None, mode: str = "bf16") -> dict:
     idt = _in_dtype_of(x)
     x, w13, w2 = (_as_input(a, idt) for a in (x, w13, w2))
     dout = _as_input(dout, idt)
-    sh = _shape(T, D, F, E, K, mode, idt)
+    sh = _shape(T, D, F, E, K, mode, idt, wgrad_f32)
     pl = plan(ids, E)
+    i13 = None if dw13_init is None else np.ascontiguousarray(dw13_init, dtype=np.float64)
+    i2 = None if dw2_init is None else np.ascontiguousarray(dw2_init, dtype=np.float64)
     ids64 = np.ascontiguousarray(ids, dtype=np.int64)
     sc = np.ascontiguousarray(scores, dtype=np.float64)
     res = dict(pl)
@@ -154,7 +159,8 @@ def full(x, ids, scores, w13, w2, dout=None, mode: str = "bf16") -> dict:
         dw2 = np.zeros((E, D, F))
         L.oracle_backward(ctypes.byref(sh), _p(dout), _p(ids64), _p(sc), _p(w13), _p(w2),
                           _p(pl["offsets"]), _p(pl["pos"]), _p(pl["src"]), _p(xg), _p(h13), _p(a),
-                          _p(y), _p(dy), _p(dscores), _p(dh13), _p(dxg), _p(dx), _p(dw13), _p(dw2))
+                          _p(y), _p(dy), _p(dscores), _p(dh13), _p(dxg), _p(dx), _p(dw13), _p(dw2),
+                          _p(i13), _p(i2))
         res.update(dy=dy, dscores=dscores, dh13=dh13, dxg=dxg, dx=dx, dw13=dw13, dw2=dw2)
     return res
 
@@ -185,22 +191,26 @@ def tokens(x, ids, scores, w13, w2, toks, dout=None, mode: str = "bf16", want_y:
 
 
 def wgrad_entries(x, ids, scores, w13, w2, dout, e: int, jd: np.ndarray, df: np.ndarray,
-                  mode: str = "bf16"):
+                  mode: str = "bf16", wgrad_f32: bool = False, init13=None, init2=None):
     """dW13[e, j, d] for the (j, d) pairs in jd ([n,2], j in [0,2F)) and dW2[e, d, f] for the
-    (d, f) pairs in df ([m,2])."""
+    (d, f) pairs in df ([m,2]); init13 / init2: existing values of those entries to accumulate
+    into."""
     T, D = x.shape
     E, _, F, _ = w13.shape
     K = ids.shape[1]
     idt = _in_dtype_of(x)
     x, w13, w2, dout = (_as_input(a, idt) for a in (x, w13, w2, dout))
-    sh = _shape(T, D, F, E, K, mode, idt)
+    sh = _shape(T, D, F, E, K, mode, idt, wgrad_f32)
     jd = np.ascontiguousarray(jd, dtype=np.int64).reshape(-1, 2)
+    i13 = None if init13 is None else np.ascontiguousarray(init13, dtype=np.float64)
+    i2 = None if init2 is None else np.ascontiguousarray(init2, dtype=np.float64)
     df = np.ascontiguousarray(df, dtype=np.int64).reshape(-1, 2)
     ids64 = np.ascontiguousarray(ids, dtype=np.int64)
     sc = np.ascontiguousarray(scores, dtype=np.float64)
     v13 = np.zeros(len(jd)); v2 = np.zeros(len(df))
     lib().oracle_wgrad_entries(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2),
-                               _p(dout), int(e), len(jd), _p(jd), _p(v13), len(df), _p(df), _p(v2))
+                               _p(dout), int(e), len(jd), _p(jd), _p(v13), len(df), _p(df), _p(v2),
+                               _p(i13), _p(i2))
     return v13, v2
 
 

@@ -48,6 +48,7 @@ typedef struct oracle_shape {
   int64_t T, D, F, E, K;
   int32_t round_bf16; /* 1: bf16 storage points; 0: exact evaluation */
   int32_t in_dtype;   /* ORACLE_IN_BF16 or ORACLE_IN_F64 for x, w13, w2, dout */
+  int32_t wgrad_f32;  /* 1: dW13, dW2 are stored in fp32 (no bf16 rounding at that point) */
 } oracle_shape;
 
 /* ------------------------------------------------------------------------------------------- */
@@ -84,6 +85,12 @@ static inline double ld(const void* p, int64_t i, int32_t dt) {
 static inline double R(const oracle_shape* s, double v) {
   return s->round_bf16 ? oracle_round_bf16(v) : v;
 }
+
+/* Storage point of a weight gradient: bf16 unless the gradients are kept in fp32 (Dist-MoE, "In-place
+ * WGRAD accumulation": gradients in BF16 or FP32, the same dtype for W13 and W2). With an initial
+ * gradient (accumulation into existing storage) the new contribution is added to it before that
+ * single rounding. */
+static inline double RW(const oracle_shape* s, double v) { return s->wgrad_f32 ? v : R(s, v); }
 
 static inline double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
@@ -272,7 +279,8 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
                     const double* scores, const void* w13, const void* w2, const int64_t* offsets,
                     const int64_t* pos, const int64_t* src, const double* xg, const double* h13,
                     const double* a, const double* y, double* dy, double* dscores, double* dh13,
-                    double* dxg, double* dx, double* dw13, double* dw2) {
+                    double* dxg, double* dx, double* dw13, double* dw2, const double* dw13_init,
+                    const double* dw2_init) {
   const int64_t T = s->T, D = s->D, F = s->F, E = s->E, K = s->K, N = T * K;
   /* dscores[t,k] = sum_d dout[t,d] * y[pos[t,k], d]; 0 for a dropped slot */
 #pragma omp parallel for schedule(static)
@@ -299,16 +307,18 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
                  dxg + r * D);
     free(drow);
   }
-  /* dW2[e,d,f] = R(sum_{r in segment e} dy[r,d] * a[r,f]), rows ascending; 0 for an empty expert */
+  /* dW2[e,d,f] = R(init + sum_{r in segment e} dy[r,d] * a[r,f]), rows ascending (init = 0 unless
+   * accumulating); an empty expert's sum is 0 */
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t e = 0; e < E; ++e)
     for (int64_t d = 0; d < D; ++d)
       for (int64_t f = 0; f < F; ++f) {
         double acc = 0.0;
         for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) acc += dy[r * D + d] * a[r * F + f];
-        dw2[(e * D + d) * F + f] = R(s, acc);
+        const int64_t o = (e * D + d) * F + f;
+        dw2[o] = RW(s, (dw2_init ? dw2_init[o] : 0.0) + acc);
       }
-  /* dW13[e,j,d] = R(sum_{r in segment e} dh13[r,j] * xg[r,d]) */
+  /* dW13[e,j,d] = R(init + sum_{r in segment e} dh13[r,j] * xg[r,d]) */
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t e = 0; e < E; ++e)
     for (int64_t j = 0; j < 2 * F; ++j)
@@ -316,7 +326,8 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
         double acc = 0.0;
         for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r)
           acc += dh13[r * 2 * F + j] * xg[r * D + d];
-        dw13[(e * 2 * F + j) * D + d] = R(s, acc);
+        const int64_t o = (e * 2 * F + j) * D + d;
+        dw13[o] = RW(s, (dw13_init ? dw13_init[o] : 0.0) + acc);
       }
   /* dx[t,d] = R(sum_k dxg[pos[t,k], d]), k ascending */
 #pragma omp parallel for schedule(static)
@@ -404,7 +415,8 @@ int oracle_tokens(const oracle_shape* s, const void* x, const int64_t* ids, cons
 int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* ids,
                          const double* scores, const void* w13, const void* w2, const void* dout,
                          int64_t e, int64_t n13, const int64_t* jd, double* dw13_vals, int64_t n2,
-                         const int64_t* df, double* dw2_vals) {
+                         const int64_t* df, double* dw2_vals, const double* dw13_init,
+                         const double* dw2_init) {
   const int64_t D = s->D, F = s->F, K = s->K, N = s->T * s->K;
   /* distinct intermediate columns f that the requested entries need */
   int64_t* fl = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n13 + n2 + 1));
@@ -447,9 +459,9 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
       }
     }
     for (int64_t p = 0; p < n2; ++p)
-      if (df[2 * p + 1] == f) dw2_vals[p] = R(s, acc2[p]);
+      if (df[2 * p + 1] == f) dw2_vals[p] = RW(s, (dw2_init ? dw2_init[p] : 0.0) + acc2[p]);
     for (int64_t p = 0; p < n13; ++p)
-      if (jd[2 * p] % F == f) dw13_vals[p] = R(s, acc13[p]);
+      if (jd[2 * p] % F == f) dw13_vals[p] = RW(s, (dw13_init ? dw13_init[p] : 0.0) + acc13[p]);
     free(acc13); free(acc2); free(xrow); free(dyrow);
   }
   free(fl);

@@ -383,3 +383,62 @@ def test_sampled_functions_agree_with_full():
                                        jd, df)
         np.testing.assert_array_equal(v13, full["dw13"][e].reshape(2 * w.F, w.D)[jd[:, 0], jd[:, 1]])
         np.testing.assert_array_equal(v2, full["dw2"][e][df[:, 0], df[:, 1]])
+
+
+# ------------------------------------------------------------------------------------------------
+# weight gradients kept in fp32, and accumulation into existing gradients (Dist-MoE, "In-place
+# WGRAD accumulation": BF16 or FP32 gradient storage, the same dtype for W13 and W2)
+
+def _bf16_values(a):
+    return np.array([oracle.round_bf16(float(v)) for v in np.ravel(a)]).reshape(np.shape(a))
+
+
+def test_wgrad_storage_modes_are_one_rounding_apart():
+    x, ids, s, w13, w2, dout = small_inputs(E=6)
+    ids[ids == 5] = 0  # expert 5 has no rows
+    ov = oracle.full(x, ids, s, w13, w2, dout)
+    f32 = oracle.full(x, ids, s, w13, w2, dout, wgrad_f32=True)
+    # the fp32 storage keeps the sum unrounded; rounding it gives the bf16 storage bit for bit
+    for k in ("dw13", "dw2"):
+        np.testing.assert_array_equal(_bf16_values(f32[k]), ov[k])
+        assert (f32[k] != ov[k]).mean() > 0.5  # most sums are not bf16 values
+    # nothing else changes
+    for k in ("out", "dx", "dscores", "dh13"):
+        np.testing.assert_array_equal(f32[k], ov[k])
+    rng = np.random.default_rng(9)
+    i13 = _bf16_values(rng.standard_normal(ov["dw13"].shape) * 0.1)
+    i2 = _bf16_values(rng.standard_normal(ov["dw2"].shape) * 0.1)
+    # accumulating onto zeros is the overwrite
+    z = oracle.full(x, ids, s, w13, w2, dout, dw13_init=np.zeros_like(i13), dw2_init=np.zeros_like(i2))
+    for k in ("dw13", "dw2"):
+        np.testing.assert_array_equal(z[k], ov[k])
+    # bf16 accumulation rounds once, after adding the unrounded contribution to the old value
+    acc = oracle.full(x, ids, s, w13, w2, dout, dw13_init=i13, dw2_init=i2)
+    for k, init in (("dw13", i13), ("dw2", i2)):
+        np.testing.assert_array_equal(acc[k], _bf16_values(init + f32[k]))
+        double_rounded = _bf16_values(init + ov[k])
+        assert (acc[k] != double_rounded).any()  # a second rounding would be visible
+    # an expert without rows keeps its old gradient
+    np.testing.assert_array_equal(acc["dw13"][5], i13[5])
+    np.testing.assert_array_equal(acc["dw2"][5], i2[5])
+    # fp32 accumulation twice adds the contribution twice
+    a1 = oracle.full(x, ids, s, w13, w2, dout, wgrad_f32=True, dw13_init=i13, dw2_init=i2)
+    a2 = oracle.full(x, ids, s, w13, w2, dout, wgrad_f32=True, dw13_init=a1["dw13"], dw2_init=a1["dw2"])
+    for k, init in (("dw13", i13), ("dw2", i2)):
+        np.testing.assert_allclose(a2[k], init + 2 * f32[k], rtol=0, atol=1e-12)
+
+
+def test_sampled_wgrad_entries_follow_the_storage_mode():
+    w = W.PARITY_WORKLOADS["p_skew"].with_(T=60)
+    inp = W.make_inputs(w)
+    full = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, wgrad_f32=True)
+    e = int(np.argmax(full["counts"]))
+    jd = np.array([[0, 0], [w.F + 3, 17], [2 * w.F - 1, w.D - 1]])
+    df = np.array([[1, 2], [w.D - 1, w.F - 1]])
+    i13 = np.array([0.25, -1.5, 3.0])
+    i2 = np.array([0.125, 7.0])
+    v13, v2 = oracle.wgrad_entries(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e, jd, df,
+                                   wgrad_f32=True, init13=i13, init2=i2)
+    np.testing.assert_allclose(v13, i13 + full["dw13"][e].reshape(2 * w.F, w.D)[jd[:, 0], jd[:, 1]],
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(v2, i2 + full["dw2"][e][df[:, 0], df[:, 1]], rtol=0, atol=1e-12)
