@@ -248,6 +248,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large_hidden")
+    ap.add_argument("--wgrad", default="bf16", choices=["bf16", "bf16-accumulate", "f32", "f32-accumulate"],
+                    help="weight-gradient storage: bf16 or fp32, overwritten or accumulated into")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=512,
                     help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--summarize", nargs=2, metavar=("RUN_DIR", "OUT_MD"),
@@ -306,7 +308,9 @@ def main():
     x, w13, w2, dout = (dv.to_device_bits(a) for a in (inp.x, inp.w13, inp.w2, inp.dout))
     ids = torch.from_numpy(inp.ids).cuda()
     scores = torch.from_numpy(inp.scores).cuda()
-    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=True)
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=True,
+                     wgrad_accumulate=args.wgrad.endswith("accumulate"),
+                     wgrad_f32=args.wgrad.startswith("f32"))
     stream = torch.cuda.current_stream().cuda_stream
     hip = HipEvents()
 
@@ -378,6 +382,30 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
+    # the router on this workload's token and expert counts (N(0,1) logits, softmax top-K,
+    # renormalised): HBM-bound on logits read plus ids and weights written
+    import mixture_experts_routed_plan_amd as M
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    logits = torch.randn(w.T, w.E, device="cuda", generator=g)
+    r_ids = torch.empty(w.T, w.K, dtype=torch.int64, device="cuda")
+    r_sc = torch.empty(w.T, w.K, dtype=torch.float32, device="cuda")
+    r_shape = M.make_shape(w.T, w.D, w.F, w.E, w.K)
+    r_cfg = M.make_router()
+    M.check(M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream), "moe_route")
+    r0, r1 = hip.create(), hip.create()
+    torch.cuda.synchronize()
+    hip.record(r0, stream)
+    for _ in range(20):
+        M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream)
+    hip.record(r1, stream)
+    torch.cuda.synchronize()
+    r_ms = hip.ms(r0, r1) / 20
+    r_bytes = 4 * w.T * w.E + 12 * w.T * w.K
+    router = {"ms": round(r_ms, 4), "gbs": round(r_bytes / r_ms / 1e6, 1),
+              "frac_peak": round(r_bytes / r_ms / 1e6 / PEAK_HBM_GBS, 4),
+              "config": "softmax top-%d of %d, renormalised, %d tokens" % (w.K, w.E, w.T)}
+
     flops = 18 * w.N * w.D * w.F
     res = {
         "metric": METRIC,
@@ -396,9 +424,11 @@ def main():
         "config": {"workload": "%s: T=%d D=%d F=%d E=%d K=%d, plan+forward+backward"
                                % (w.name, w.T, w.D, w.F, w.E, w.K),
                    "T": w.T, "D": w.D, "F": w.F, "E": w.E, "K": w.K,
-                   "routing": w.routing, "parallelism": "single GPU (one EP rank's share)"},
+                   "routing": w.routing, "wgrad": args.wgrad,
+                   "parallelism": "single GPU (one EP rank's share)"},
         "roofline": roof,
         "stages": stages,
+        "router": router,
     }
     hip.close()
     if args.cpu_baseline_tokens > 0:

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* moe_shape.ids_dtype */
 #define MOE_IDS_I32 0
@@ -73,6 +73,14 @@ extern "C" {
  * moe_backward can run. Without it the forward keeps its intermediates in the workspace and
  * stores no h13. */
 #define MOE_SAVE_FOR_BACKWARD 1
+/* Weight-gradient storage (Dist-MoE, "In-place WGRAD accumulation": gradients accumulate into
+ * existing parameter-gradient storage, which is BF16 or FP32, the same dtype for W13 and W2):
+ *   MOE_WGRAD_ACCUMULATE: moe_backward adds its dW13, dW2 to the values already in dw13, dw2
+ *     (the new contribution, summed in fp32, is added to the old value in fp32 and the sum is
+ *     stored: one rounding in bf16 storage); without it dw13, dw2 are overwritten.
+ *   MOE_WGRAD_F32: dw13, dw2 are fp32 arrays (float, same shapes); without it bf16. */
+#define MOE_WGRAD_ACCUMULATE 2
+#define MOE_WGRAD_F32 4
 
 /* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64,
  * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31. */
@@ -151,11 +159,14 @@ moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t*
  *   dxg[r]      = bf16(w13[e]^T . dh13[r])                (w13[e] viewed as [2F,D])
  *   dw13[e]     = bf16(sum over e's rows of dh13^T xg)
  *   dx[t]       = bf16(sum_k dxg[pos[t*K+k]])             (k ascending, fp32)
- * dx, dw13 and dw2 are overwritten. Requires the shape's MOE_SAVE_FOR_BACKWARD and the saved
+ * dx is overwritten; dw13 and dw2 are overwritten or accumulated into, bf16 or fp32, as the shape's
+ * MOE_WGRAD_* flags say (the accumulation of a call is not atomic with respect to other work on the
+ * same buffers: calls that accumulate into one buffer must be ordered, e.g. on one stream).
+ * Requires the shape's MOE_SAVE_FOR_BACKWARD and the saved
  * buffer of the matching forward; workspace holds dy/dxg and dh13. */
 moe_status moe_backward(const moe_shape* shape, const void* plan, const void* saved,
                         const uint16_t* dout, const float* scores, const uint16_t* w13,
-                        const uint16_t* w2, uint16_t* dx, uint16_t* dw13, uint16_t* dw2,
+                        const uint16_t* w2, uint16_t* dx, void* dw13, void* dw2,
                         float* dscores, void* workspace, hipStream_t stream,
                         const moe_trace* trace);
 

@@ -13,7 +13,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
   if (s->ids_dtype != MOE_IDS_I32 && s->ids_dtype != MOE_IDS_I64) return MOE_E_DTYPE;
-  if (s->flags & ~MOE_SAVE_FOR_BACKWARD) return MOE_E_DTYPE;
+  if (s->flags & ~(MOE_SAVE_FOR_BACKWARD | MOE_WGRAD_ACCUMULATE | MOE_WGRAD_F32)) return MOE_E_DTYPE;
   if (s->T < 1 || s->K < 1 || s->K > MOE_MAX_TOPK) return MOE_E_SHAPE;
   if (s->E < 1 || s->E > MOE_MAX_EXPERTS) return MOE_E_SHAPE;
   if (s->D < 64 || s->F < 64 || (s->D % 64) != 0 || (s->F % 64) != 0) return MOE_E_SHAPE;
@@ -140,7 +140,7 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
 
 moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
                         const uint16_t* dout, const float* scores, const uint16_t* w13,
-                        const uint16_t* w2, uint16_t* dx, uint16_t* dw13, uint16_t* dw2,
+                        const uint16_t* w2, uint16_t* dx, void* dw13, void* dw2,
                         float* dscores, void* workspace, hipStream_t stream,
                         const moe_trace* trace) {
   moe_status st = check_shape(s);

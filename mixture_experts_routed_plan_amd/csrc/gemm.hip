@@ -54,6 +54,8 @@ constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+// EPI_STORE output: bf16 (C), bf16 added to the existing values, fp32 (Cf), fp32 added
+enum { OUT_BF16 = 0, OUT_BF16_ACC = 1, OUT_F32 = 2, OUT_F32_ACC = 3 };
 enum { SCHED_ROWS = 0, SCHED_KSEG = 1 };
 
 struct GemmArgs {
@@ -63,6 +65,7 @@ struct GemmArgs {
   int64_t ldq;
   int64_t q_estride;  // elements between experts in Q (weights); 0 when Q is not per expert
   uint16_t* C;        // output (EPI_STORE), h13 (EPI_SWIGLU_FWD, may be null), dh13 (BWD)
+  float* Cf;          // fp32 output (EPI_STORE with OUT_F32 / OUT_F32_ACC), same ldc / c_estride
   int64_t ldc;
   int64_t c_estride;  // elements between experts in C (WGRAD outputs)
   uint16_t* C2;       // a (EPI_SWIGLU_FWD)
@@ -266,7 +269,7 @@ __device__ __forceinline__ v4i16 read_mn_half(const uint16_t* tile, int idx0, in
 
 // ---- the kernel -------------------------------------------------------------------------------
 
-template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI>
+template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI, int OUT = OUT_BF16>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   static_assert(BM == 256 && BN == 256, "the interleaved schedule below assumes 256x256 tiles");
@@ -498,7 +501,80 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         *(uint4*)(dst + (int64_t)r * ld + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE && OUT != OUT_BF16) {
+    // fp32 staging ([32][WN + 4] floats per wavefront), then per 8 consecutive outputs of a row:
+    // optionally the existing values added in fp32, then one rounding (bf16) or none (fp32)
+    constexpr int PW = WN + 4;
+    static_assert(32 * PW * 4 <= kEpWaveElems * 2, "fp32 staging area");
+    float* epf = (float*)ep;
+    const int64_t cofs = (int64_t)t.e * g.c_estride;
+    constexpr int per_row = WN / 8, rows_per_pass = 64 / per_row;
+    constexpr int NP = 32 / rows_per_pass;  // flush passes per 32-row block
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      if (j >= jlim) break;
+      const int row0 = t.r0 + wr * WM + j * 32, col0 = t.n0 + wc * WN;
+      // the existing values this lane adds to, loaded before the staging so that their latency
+      // overlaps it
+      uint4 oldb[OUT == OUT_BF16_ACC ? NP : 1];
+      float4 oldf[OUT == OUT_F32_ACC ? 2 * NP : 1];
+      if constexpr (OUT == OUT_BF16_ACC || OUT == OUT_F32_ACC) {
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          const int r = row0 + pass * rows_per_pass + lane / per_row;
+          const int c = col0 + (lane % per_row) * 8;
+          const bool in = r < t.r_lim && c < g.N_out;
+          const int64_t o = cofs + (int64_t)(in ? r : 0) * g.ldc + (in ? c : 0);
+          if constexpr (OUT == OUT_BF16_ACC) {
+            oldb[pass] = *(const uint4*)(g.C + o);
+          } else {
+            oldf[2 * pass] = *(const float4*)(g.Cf + o);
+            oldf[2 * pass + 1] = *(const float4*)(g.Cf + o + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *(float4*)(epf + rl * PW + i * 32 + gq * 8 + cq) =
+              make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                          acc[i][j][4 * gq + 3]);
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
+        const float* src = epf + row * PW + ch * 8;
+        float v[8];
+        *(float4*)&v[0] = *(const float4*)src;
+        *(float4*)&v[4] = *(const float4*)(src + 4);
+        const int r = row0 + row, c = col0 + ch * 8;
+        if (r < t.r_lim && c < g.N_out) {
+          const int64_t o = cofs + (int64_t)r * g.ldc + c;
+          if constexpr (OUT == OUT_BF16_ACC) {
+            const uint4 old = oldb[pass];
+            const uint32_t w[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v[2 * q] += bf16_to_f32(w[q] & 0xffffu);
+              v[2 * q + 1] += bf16_to_f32(w[q] >> 16);
+            }
+            *(uint4*)(g.C + o) = make_uint4(pk2(v[0], v[1]), pk2(v[2], v[3]), pk2(v[4], v[5]),
+                                            pk2(v[6], v[7]));
+          } else {
+            float4* d = (float4*)(g.Cf + o);
+            float4 a = *(const float4*)&v[0], b = *(const float4*)&v[4];
+            if constexpr (OUT == OUT_F32_ACC) {
+              const float4 oa = oldf[2 * pass], ob = oldf[2 * pass + 1];
+              a.x += oa.x; a.y += oa.y; a.z += oa.z; a.w += oa.w;
+              b.x += ob.x; b.y += ob.y; b.z += ob.z; b.w += ob.w;
+            }
+            d[0] = a;
+            d[1] = b;
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE) {
     uint16_t* C = g.C + (int64_t)t.e * g.c_estride;
     constexpr int PW = WN + 4;
 #pragma unroll
@@ -614,6 +690,31 @@ MOE_GEMM_KERNEL(moe_dgrad_w13, true, false, SCHED_ROWS, EPI_STORE)
 MOE_GEMM_KERNEL(moe_wgrad_w2, false, false, SCHED_KSEG, EPI_STORE)
 MOE_GEMM_KERNEL(moe_wgrad_w13, false, false, SCHED_KSEG, EPI_STORE)
 
+// weight gradients accumulated into existing storage, or kept in fp32
+#define MOE_WGRAD_KERNEL(name, OUT)                                                             \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void name( \
+      GemmArgs g) {                                                                            \
+    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(g);                          \
+  }
+
+MOE_WGRAD_KERNEL(moe_wgrad_w2_accum, OUT_BF16_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w2_f32, OUT_F32)
+MOE_WGRAD_KERNEL(moe_wgrad_w2_f32_accum, OUT_F32_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_accum, OUT_BF16_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_f32, OUT_F32)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_f32_accum, OUT_F32_ACC)
+
+// kernel of a weight-gradient GEMM for the shape's storage flags
+void (*wgrad_kernel(const moe_shape& s, bool w13))(GemmArgs) {
+  const bool acc = (s.flags & MOE_WGRAD_ACCUMULATE) != 0, f32 = (s.flags & MOE_WGRAD_F32) != 0;
+  if (w13) {
+    if (f32) return acc ? moe_wgrad_w13_f32_accum : moe_wgrad_w13_f32;
+    return acc ? moe_wgrad_w13_accum : moe_wgrad_w13;
+  }
+  if (f32) return acc ? moe_wgrad_w2_f32_accum : moe_wgrad_w2_f32;
+  return acc ? moe_wgrad_w2_accum : moe_wgrad_w2;
+}
+
 hipError_t launch(void (*kernel)(GemmArgs), const GemmArgs& g, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, g);
@@ -686,27 +787,27 @@ hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
 }
 
 hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* a, uint16_t* dw2, hipStream_t st) {
+                           const uint16_t* a, void* dw2, hipStream_t st) {
   GemmArgs g{};
   g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
   g.P = dy; g.ldp = s.D;  // [k = routed row][r = d]
   g.Q = a; g.ldq = s.F;   // [k = routed row][c = f]
-  g.C = dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
+  g.C = (uint16_t*)dw2; g.Cf = (float*)dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
   g.M_out = (int)s.D; g.N_out = (int)s.F;
   const int grid = (int)(s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN));
-  return launch(moe_wgrad_w2, g, grid, st);
+  return launch(wgrad_kernel(s, false), g, grid, st);
 }
 
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
-                            const uint16_t* xg, uint16_t* dw13, hipStream_t st) {
+                            const uint16_t* xg, void* dw13, hipStream_t st) {
   GemmArgs g{};
   g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
   g.P = dh13; g.ldp = 2 * s.F;  // [k = routed row][r = j]
   g.Q = xg; g.ldq = s.D;        // [k = routed row][c = d]
-  g.C = dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
+  g.C = (uint16_t*)dw13; g.Cf = (float*)dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
   g.M_out = (int)(2 * s.F); g.N_out = (int)s.D;
   const int grid = (int)(s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN));
-  return launch(moe_wgrad_w13, g, grid, st);
+  return launch(wgrad_kernel(s, true), g, grid, st);
 }
 
 }  // namespace moe

@@ -173,11 +173,12 @@ hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
 hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
                            const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
                            hipStream_t st);
+// weight gradients: bf16 or fp32 storage, overwritten or accumulated (shape flags)
 hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* a, uint16_t* dw2, hipStream_t st);
+                           const uint16_t* a, void* dw2, hipStream_t st);
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st);
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
-                            const uint16_t* xg, uint16_t* dw13, hipStream_t st);
+                            const uint16_t* xg, void* dw13, hipStream_t st);
 
 }  // namespace moe

@@ -28,10 +28,10 @@ class Layer:
     """Buffers and calls for one shape. Inputs are device tensors owned by the caller."""
 
     def __init__(self, T, D, F, E, K, ids_dtype=np.int64, save_for_backward=True,
-                 device="cuda", alloc_grads=None):
+                 device="cuda", alloc_grads=None, wgrad_accumulate=False, wgrad_f32=False):
         self.shape = make_shape(T, D, F, E, K,
                                 MOE_IDS_I64 if np.dtype(ids_dtype) == np.int64 else MOE_IDS_I32,
-                                save_for_backward)
+                                save_for_backward, wgrad_accumulate, wgrad_f32)
         s = self.shape
         self.device = device
         nb = moe_plan_bytes(s)
@@ -46,8 +46,11 @@ class Layer:
             alloc_grads = save_for_backward
         if alloc_grads:
             self.dx = torch.empty(T, D, dtype=torch.bfloat16, device=device)
-            self.dw13 = torch.empty(E, 2, F, D, dtype=torch.bfloat16, device=device)
-            self.dw2 = torch.empty(E, D, F, dtype=torch.bfloat16, device=device)
+            gdt = torch.float32 if wgrad_f32 else torch.bfloat16
+            # accumulation reads the existing gradients: start from zeros
+            mk = torch.zeros if wgrad_accumulate else torch.empty
+            self.dw13 = mk(E, 2, F, D, dtype=gdt, device=device)
+            self.dw2 = mk(E, D, F, dtype=gdt, device=device)
             self.dscores = torch.empty(T, K, dtype=torch.float32, device=device)
 
     # -- calls -----------------------------------------------------------------------------

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 1
+    assert M.moe_abi_version() == 2
     for st in range(0, -8, -1):
         assert M.moe_status_str(st) != "unknown status"
     assert M.moe_status_str(-99) == "unknown status"
@@ -80,8 +80,12 @@ def test_bad_dtype_and_flags_rejected():
     s.ids_dtype = 7
     assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_DTYPE
     s = shape()
-    s.flags = 6
+    s.flags = 8
     assert M.moe_plan_bytes(s) == 0
+    s2 = shape()
+    s2.flags = M.MOE_SAVE_FOR_BACKWARD | M.MOE_WGRAD_ACCUMULATE | M.MOE_WGRAD_F32
+    assert M.moe_plan_bytes(s2) > 0
+    s.flags = 8
     assert M.moe_forward(s, 256, 256, 256, 256, 256, 256, 256, 256, 0) == M.MOE_E_DTYPE
 
 
