@@ -72,6 +72,8 @@ PLAN_STAGES = ["plan_hist", "plan_scan", "plan_scatter"]
 FWD_STAGES = ["permute", "fprop_w13_swiglu", "fprop_w2", "combine"]
 BWD_STAGES = ["combine_bwd_dscores", "dgrad_w2_swiglu", "wgrad_w2", "dgrad_w13", "wgrad_w13",
               "dx_combine"]
+# with --recompute the backward rebuilds h13 and a first (one more gate/up GEMM)
+BWD_STAGES_RECOMPUTE = BWD_STAGES[:1] + ["recompute_w13"] + BWD_STAGES[1:]
 
 
 def stage_work(w):
@@ -80,6 +82,7 @@ def stage_work(w):
     return {
         "permute": ("hbm", 2 * T * D + 2 * N * D),
         "fprop_w13_swiglu": ("mfma", 4 * N * D * F),
+        "recompute_w13": ("mfma", 4 * N * D * F),
         "fprop_w2": ("mfma", 2 * N * D * F),
         "combine": ("hbm", 2 * N * D + 2 * T * D),
         "combine_bwd_dscores": ("hbm", 2 * T * D + 4 * N * D),
@@ -125,7 +128,7 @@ STAGE_KERNEL = {
     "fprop_w2": "moe_fprop_w2", "combine": "moe_combine<true>",
     "combine_bwd_dscores": "moe_combine_bwd_dscores", "dgrad_w2_swiglu": "moe_dgrad_w2_swiglu",
     "wgrad_w2": "moe_wgrad_w2", "dgrad_w13": "moe_dgrad_w13", "wgrad_w13": "moe_wgrad_w13",
-    "dx_combine": "moe_combine<false>",
+    "dx_combine": "moe_combine<false>", "recompute_w13": "moe_fprop_w13_swiglu",
 }
 
 
@@ -248,6 +251,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large_hidden")
+    ap.add_argument("--recompute", action="store_true",
+                    help="save only xg and y; the backward recomputes h13 and a")
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "bf16-accumulate", "f32", "f32-accumulate"],
                     help="weight-gradient storage: bf16 or fp32, overwritten or accumulated into")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=512,
@@ -310,7 +315,8 @@ def main():
     scores = torch.from_numpy(inp.scores).cuda()
     layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=True,
                      wgrad_accumulate=args.wgrad.endswith("accumulate"),
-                     wgrad_f32=args.wgrad.startswith("f32"))
+                     wgrad_f32=args.wgrad.startswith("f32"), recompute=args.recompute)
+    bwd_stages = BWD_STAGES_RECOMPUTE if args.recompute else BWD_STAGES
     stream = torch.cuda.current_stream().cuda_stream
     hip = HipEvents()
 
@@ -333,7 +339,8 @@ def main():
     torch.cuda.synchronize()
     log("bench: %d warmup steps done" % args.warmup)
 
-    traces = [(make_trace(4), make_trace(5), make_trace(7)) for _ in range(args.steps)]
+    traces = [(make_trace(4), make_trace(5), make_trace(len(bwd_stages) + 1))
+              for _ in range(args.steps)]
     start, end = hip.create(), hip.create()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -348,10 +355,10 @@ def main():
     log("bench: %d timed steps, %.3f ms/step (wall %.3f ms/step)" %
         (args.steps, ms, 1e3 * wall / args.steps))
 
-    names = PLAN_STAGES + FWD_STAGES + BWD_STAGES
+    names = PLAN_STAGES + FWD_STAGES + bwd_stages
     per = {n: [] for n in names}
     for (tp, ep), (tf, ef), (tb, eb) in traces:
-        for lst, evs in ((PLAN_STAGES, ep), (FWD_STAGES, ef), (BWD_STAGES, eb)):
+        for lst, evs in ((PLAN_STAGES, ep), (FWD_STAGES, ef), (bwd_stages, eb)):
             for i, n in enumerate(lst):
                 per[n].append(hip.ms(evs[i], evs[i + 1]))
     work = stage_work(w)
@@ -368,7 +375,7 @@ def main():
                 ent["gbs"] = round(amount / avg / 1e6, 1)
                 ent["frac_peak"] = round(amount / avg / 1e6 / PEAK_HBM_GBS, 4)
         stages[n] = ent
-    dom = max(work, key=lambda n: stages[n]["ms"])
+    dom = max((n for n in work if n in stages), key=lambda n: stages[n]["ms"])
     kind, amount = work[dom]
     avg_s = stages[dom]["ms"] / 1e3
     if kind == "mfma":
@@ -424,7 +431,7 @@ def main():
         "config": {"workload": "%s: T=%d D=%d F=%d E=%d K=%d, plan+forward+backward"
                                % (w.name, w.T, w.D, w.F, w.E, w.K),
                    "T": w.T, "D": w.D, "F": w.F, "E": w.E, "K": w.K,
-                   "routing": w.routing, "wgrad": args.wgrad,
+                   "routing": w.routing, "wgrad": args.wgrad, "recompute": args.recompute,
                    "parallelism": "single GPU (one EP rank's share)"},
         "roofline": roof,
         "stages": stages,

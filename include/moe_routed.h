@@ -81,6 +81,14 @@ extern "C" {
  *   MOE_WGRAD_F32: dw13, dw2 are fp32 arrays (float, same shapes); without it bf16. */
 #define MOE_WGRAD_ACCUMULATE 2
 #define MOE_WGRAD_F32 4
+/* Recompute instead of saving (TeraMoE introduction and activation-memory table: the fused
+ * kernel trades recomputation for activation memory; Dist-MoE "Use graph and checkpoint
+ * features": recompute under a fixed launch sequence). With MOE_SAVE_FOR_BACKWARD | MOE_RECOMPUTE
+ * the forward keeps only xg and y in the saved buffer (its a goes to the workspace, which the
+ * forward then needs), and moe_backward recomputes h13 and a from xg with the same kernel before
+ * the backward proper: the same bits as the saved ones, so every output is bitwise the one of the
+ * saving path, for one more gate/up GEMM. */
+#define MOE_RECOMPUTE 8
 
 /* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64,
  * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31. */
@@ -124,7 +132,8 @@ typedef struct moe_trace {
 /* Byte sizes of the caller-allocated buffers; 0 for a shape that fails the checks. */
 size_t moe_plan_bytes(const moe_shape* shape);
 size_t moe_saved_bytes(const moe_shape* shape);     /* 0 unless MOE_SAVE_FOR_BACKWARD */
-size_t moe_workspace_bytes(const moe_shape* shape); /* forward without save, and backward */
+size_t moe_workspace_bytes(const moe_shape* shape); /* forward without save or with recompute,
+                                                      and backward */
 
 /* Routing plan (Dist-MoE, "Understand the execution model": routing metadata is generated on the
  * GPU from caller ids; TeraMoE README: the scheduler forms per-expert batches).
@@ -181,7 +190,8 @@ moe_status moe_plan_status(const moe_shape* shape, const void* plan, int64_t* ba
                            hipStream_t stream);
 
 /* Device pointers to the saved forward intermediates inside saved (for inspection and tests):
- * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. */
+ * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. With MOE_RECOMPUTE
+ * h13 and a are not saved: *h13 and *a are set to NULL. */
 moe_status moe_saved_views(const moe_shape* shape, void* saved, uint16_t** xg, uint16_t** h13,
                            uint16_t** a, uint16_t** y);
 

@@ -19,6 +19,7 @@ MOE_IDS_I64 = 1
 MOE_SAVE_FOR_BACKWARD = 1
 MOE_WGRAD_ACCUMULATE = 2
 MOE_WGRAD_F32 = 4
+MOE_RECOMPUTE = 8
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_TRACE_MAX_EVENTS = 8
@@ -120,9 +121,10 @@ def _stream(stream):
 
 
 def make_shape(T, D, F, E, K, ids_dtype=MOE_IDS_I64, save_for_backward=True,
-               wgrad_accumulate=False, wgrad_f32=False) -> moe_shape:
+               wgrad_accumulate=False, wgrad_f32=False, recompute=False) -> moe_shape:
     flags = ((MOE_SAVE_FOR_BACKWARD if save_for_backward else 0)
-             | (MOE_WGRAD_ACCUMULATE if wgrad_accumulate else 0) | (MOE_WGRAD_F32 if wgrad_f32 else 0))
+             | (MOE_WGRAD_ACCUMULATE if wgrad_accumulate else 0) | (MOE_WGRAD_F32 if wgrad_f32 else 0)
+             | (MOE_RECOMPUTE if recompute else 0))
     return moe_shape(int(T), int(D), int(F), int(E), int(K), int(ids_dtype), flags)
 
 

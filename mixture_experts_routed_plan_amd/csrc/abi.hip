@@ -13,7 +13,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
   if (s->ids_dtype != MOE_IDS_I32 && s->ids_dtype != MOE_IDS_I64) return MOE_E_DTYPE;
-  if (s->flags & ~(MOE_SAVE_FOR_BACKWARD | MOE_WGRAD_ACCUMULATE | MOE_WGRAD_F32)) return MOE_E_DTYPE;
+  if (s->flags & ~(MOE_SAVE_FOR_BACKWARD | MOE_WGRAD_ACCUMULATE | MOE_WGRAD_F32 | MOE_RECOMPUTE))
+    return MOE_E_DTYPE;
   if (s->T < 1 || s->K < 1 || s->K > MOE_MAX_TOPK) return MOE_E_SHAPE;
   if (s->E < 1 || s->E > MOE_MAX_EXPERTS) return MOE_E_SHAPE;
   if (s->D < 64 || s->F < 64 || (s->D % 64) != 0 || (s->F % 64) != 0) return MOE_E_SHAPE;
@@ -102,8 +103,10 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool save = (s->flags & MOE_SAVE_FOR_BACKWARD) != 0;
+  const bool re = save && (s->flags & MOE_RECOMPUTE) != 0;
   if (!plan || !x || !scores || !w13 || !w2 || !out) return MOE_E_NULL;
   if (save ? !saved : !workspace) return MOE_E_NULL;
+  if (re && !workspace) return MOE_E_NULL;
   if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
       !aligned(out, 16) || !aligned(scores, 4) || (saved && !aligned(saved, 16)) ||
       (workspace && !aligned(workspace, 16)))
@@ -115,9 +118,13 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
     const SavedLayout S = saved_layout(*s);
     char* b = (char*)saved;
     xg = (uint16_t*)(b + S.xg);
-    h13 = (uint16_t*)(b + S.h13);
-    a = (uint16_t*)(b + S.a);
     y = (uint16_t*)(b + S.y);
+    if (re) {  // h13 is not kept; a lives in the workspace until W2 has read it
+      a = (uint16_t*)((char*)workspace + work_layout(*s).a);
+    } else {
+      h13 = (uint16_t*)(b + S.h13);
+      a = (uint16_t*)(b + S.a);
+    }
   } else {
     const WorkLayout W = work_layout(*s);
     char* b = (char*)workspace;
@@ -155,21 +162,28 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
     return MOE_E_ALIGN;
   const PlanLayout L = plan_layout(*s);
   const PlanPtrs p = plan_ptrs(L, (void*)plan);
+  const bool re = (s->flags & MOE_RECOMPUTE) != 0;
   const SavedLayout S = saved_layout(*s);
   const char* sb = (const char*)saved;
-  const uint16_t* xg = (const uint16_t*)(sb + S.xg);
-  const uint16_t* h13 = (const uint16_t*)(sb + S.h13);
-  const uint16_t* a = (const uint16_t*)(sb + S.a);
-  const uint16_t* y = (const uint16_t*)(sb + S.y);
   const WorkLayout W = work_layout(*s);
   char* wb = (char*)workspace;
+  const uint16_t* xg = (const uint16_t*)(sb + S.xg);
+  const uint16_t* y = (const uint16_t*)(sb + S.y);
   uint16_t* dy = (uint16_t*)(wb + W.dy);
   uint16_t* dh13 = (uint16_t*)(wb + W.dh13);
   uint16_t* dxg = dy;  // dy is dead once the W2 weight gradient has been formed
+  // recompute: h13 is rebuilt where dh13 goes (read and overwritten element by element by the
+  // SwiGLU-derivative GEMM), a in its own workspace region
+  const uint16_t* h13 = re ? dh13 : (const uint16_t*)(sb + S.h13);
+  const uint16_t* a = re ? (const uint16_t*)(wb + W.a_re) : (const uint16_t*)(sb + S.a);
   Tracer tr{trace, stream, 0};
   MOE_TRY(tr.mark());
   MOE_TRY(launch_combine_bwd(*s, p.pos, dout, y, scores, dy, dscores, stream));
   MOE_TRY(tr.mark());
+  if (re) {
+    MOE_TRY(launch_fprop_w13(*s, p, xg, w13, dh13, (uint16_t*)(wb + W.a_re), stream));
+    MOE_TRY(tr.mark());
+  }
   MOE_TRY(launch_dgrad_w2(*s, p, dy, w2, h13, dh13, stream));
   MOE_TRY(tr.mark());
   MOE_TRY(launch_wgrad_w2(*s, p, dy, a, dw2, stream));
@@ -248,9 +262,10 @@ moe_status moe_saved_views(const moe_shape* s, void* saved, uint16_t** xg, uint1
   if (!saved) return MOE_E_NULL;
   const SavedLayout S = saved_layout(*s);
   char* b = (char*)saved;
+  const bool re = (s->flags & MOE_RECOMPUTE) != 0;
   if (xg) *xg = (uint16_t*)(b + S.xg);
-  if (h13) *h13 = (uint16_t*)(b + S.h13);
-  if (a) *a = (uint16_t*)(b + S.a);
+  if (h13) *h13 = re ? nullptr : (uint16_t*)(b + S.h13);
+  if (a) *a = re ? nullptr : (uint16_t*)(b + S.a);
   if (y) *y = (uint16_t*)(b + S.y);
   return MOE_OK;
 }

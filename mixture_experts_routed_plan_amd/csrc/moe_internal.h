@@ -57,9 +57,12 @@ struct SavedLayout {
   size_t xg, h13, a, y, total;
 };
 
+// With MOE_RECOMPUTE only xg and y are saved (h13 and a are recomputed in the backward); the
+// h13 and a offsets are then unused.
 inline SavedLayout saved_layout(const moe_shape& s) {
   SavedLayout L{};
   const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
+  const bool re = (s.flags & MOE_RECOMPUTE) != 0;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -67,18 +70,20 @@ inline SavedLayout saved_layout(const moe_shape& s) {
     return at;
   };
   L.xg = take(2 * N * D);
-  L.h13 = take(2 * N * 2 * F);
-  L.a = take(2 * N * F);
+  L.h13 = re ? 0 : take(2 * N * 2 * F);
+  L.a = re ? 0 : take(2 * N * F);
   L.y = take(2 * N * D);
   L.total = o;
   return L;
 }
 
-// Workspace: the forward without saving keeps xg, a, y here; the backward keeps dy (later reused
-// for dxg, once dy is dead) and dh13.
+// Workspace: the forward without saving keeps xg, a, y here (with MOE_RECOMPUTE only a); the
+// backward keeps dy (later reused for dxg, once dy is dead) and dh13; with MOE_RECOMPUTE also the
+// recomputed a (a_re), and the recomputed h13 sits where dh13 goes (the SwiGLU-derivative GEMM
+// reads each g, u and writes its dg, du in place).
 struct WorkLayout {
   size_t xg, a, y, fwd_total;
-  size_t dy, dh13, bwd_total;
+  size_t dy, dh13, a_re, bwd_total;
   size_t total;
 };
 
@@ -91,7 +96,8 @@ inline WorkLayout work_layout(const moe_shape& s) {
   L.fwd_total = L.y + align_up(2 * N * D, 256);
   L.dy = 0;
   L.dh13 = align_up(2 * N * D, 256);
-  L.bwd_total = L.dh13 + align_up(2 * N * 2 * F, 256);
+  L.a_re = L.dh13 + align_up(2 * N * 2 * F, 256);
+  L.bwd_total = (s.flags & MOE_RECOMPUTE) ? L.a_re + align_up(2 * N * F, 256) : L.a_re;
   L.total = L.fwd_total > L.bwd_total ? L.fwd_total : L.bwd_total;
   return L;
 }

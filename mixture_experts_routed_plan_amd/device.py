@@ -28,10 +28,11 @@ class Layer:
     """Buffers and calls for one shape. Inputs are device tensors owned by the caller."""
 
     def __init__(self, T, D, F, E, K, ids_dtype=np.int64, save_for_backward=True,
-                 device="cuda", alloc_grads=None, wgrad_accumulate=False, wgrad_f32=False):
+                 device="cuda", alloc_grads=None, wgrad_accumulate=False, wgrad_f32=False,
+                 recompute=False):
         self.shape = make_shape(T, D, F, E, K,
                                 MOE_IDS_I64 if np.dtype(ids_dtype) == np.int64 else MOE_IDS_I32,
-                                save_for_backward, wgrad_accumulate, wgrad_f32)
+                                save_for_backward, wgrad_accumulate, wgrad_f32, recompute)
         s = self.shape
         self.device = device
         nb = moe_plan_bytes(s)
@@ -93,6 +94,8 @@ class Layer:
         out = {}
         for name, addr, cols in (("xg", xg, s.D), ("h13", h13, 2 * s.F), ("a", a, s.F),
                                  ("y", y, s.D)):
+            if addr is None:  # not saved (recompute)
+                continue
             off = addr - base
             t = self.saved[off:off + 2 * N * cols].view(torch.int16).view(N, cols)
             out[name] = t.cpu().numpy().view(np.uint16)

@@ -61,6 +61,10 @@ def test_sizes_are_closed_forms_of_the_shape():
     assert M.moe_saved_bytes(s) >= 2 * N * (256 + 2 * 128 + 128 + 256)
     assert M.moe_workspace_bytes(s) >= 2 * N * (256 + 2 * 128)
     assert M.moe_saved_bytes(shape(save_for_backward=False)) == 0
+    # recompute keeps only xg and y, and the backward needs room for the recomputed a
+    re = M.make_shape(64, 256, 128, 8, 2, recompute=True)
+    assert M.moe_saved_bytes(re) == M.moe_saved_bytes(s) - 2 * N * (2 * 128 + 128)
+    assert M.moe_workspace_bytes(re) >= 2 * N * (256 + 2 * 128 + 128)  # dy, h13/dh13, a
     big = shape(T=640)
     assert M.moe_plan_bytes(big) > M.moe_plan_bytes(s)
     assert M.moe_saved_bytes(big) > M.moe_saved_bytes(s)
@@ -80,12 +84,12 @@ def test_bad_dtype_and_flags_rejected():
     s.ids_dtype = 7
     assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_DTYPE
     s = shape()
-    s.flags = 8
+    s.flags = 16
     assert M.moe_plan_bytes(s) == 0
     s2 = shape()
     s2.flags = M.MOE_SAVE_FOR_BACKWARD | M.MOE_WGRAD_ACCUMULATE | M.MOE_WGRAD_F32
     assert M.moe_plan_bytes(s2) > 0
-    s.flags = 8
+    s.flags = 16
     assert M.moe_forward(s, 256, 256, 256, 256, 256, 256, 256, 256, 0) == M.MOE_E_DTYPE
 
 
@@ -103,6 +107,9 @@ def test_null_and_alignment_rejected():
     assert M.moe_forward(s, a, a, a, a, a, a, None, a, 0) == M.MOE_E_NULL
     s2 = shape(save_for_backward=False)
     assert M.moe_forward(s2, a, a, a, a, a, a, a, None, 0) == M.MOE_E_NULL
+    # with recompute the forward also needs the workspace (for a)
+    s3 = M.make_shape(64, 256, 128, 8, 2, recompute=True)
+    assert M.moe_forward(s3, a, a, a, a, a, a, a, None, 0) == M.MOE_E_NULL
     args = [a] * 11
     assert M.moe_backward(s, *args[:3], None, *args[4:11], stream=0) == M.MOE_E_NULL
     assert M.moe_backward(s2, *args, stream=0) == M.MOE_E_STATE
