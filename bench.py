@@ -389,6 +389,26 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
+    # forward only (inference; no saving, so the permute is fused into the gate/up GEMM)
+    fl = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=False, alloc_grads=False)
+    fl.plan(ids, stream)
+    for _ in range(2):
+        fl.forward(x, scores, w13, w2, stream)
+    f0, f1 = hip.create(), hip.create()
+    torch.cuda.synchronize()
+    hip.record(f0, stream)
+    for _ in range(args.steps):
+        fl.forward(x, scores, w13, w2, stream)
+    hip.record(f1, stream)
+    torch.cuda.synchronize()
+    f_ms = hip.ms(f0, f1) / args.steps
+    forward_only = {"ms": round(f_ms, 4),
+                    "tflops": round(6 * w.N * w.D * w.F / (f_ms / 1e3) / 1e12, 1),
+                    "tokens_per_s": round(w.T / (f_ms / 1e3), 1),
+                    "config": "forward without saving (permute fused into the gate/up GEMM), "
+                              "plan excluded"}
+    del fl
+
     # the router on this workload's token and expert counts (N(0,1) logits, softmax top-K,
     # renormalised): HBM-bound on logits read plus ids and weights written
     import mixture_experts_routed_plan_amd as M
@@ -436,6 +456,7 @@ def main():
         "roofline": roof,
         "stages": stages,
         "router": router,
+        "forward_only": forward_only,
     }
     hip.close()
     if args.cpu_baseline_tokens > 0:

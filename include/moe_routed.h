@@ -154,7 +154,10 @@ moe_status moe_plan(const moe_shape* shape, const void* topk_ids, void* plan, hi
  *   y[r]    = bf16(w2[e] . a[r])                             (down grouped GEMM)
  *   out[t]  = bf16(sum_k scores[t,k] * y[pos[t*K+k]])        (combine, k ascending, fp32)
  * plan: from moe_plan with the same shape and ids. saved (moe_saved_bytes) is required with
- * MOE_SAVE_FOR_BACKWARD, workspace (moe_workspace_bytes) without it; the other may be NULL. */
+ * MOE_SAVE_FOR_BACKWARD, workspace (moe_workspace_bytes) without it; the other may be NULL.
+ * Without MOE_SAVE_FOR_BACKWARD (and when x spans less than 4 GiB) the permute is fused into the
+ * gate/up GEMM, which reads each routed row's token row of x directly (MoonEP FAQ: tokens go
+ * straight to their expert-grouped positions); xg is then never materialized. */
 moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t* x,
                        const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
                        void* saved, void* workspace, hipStream_t stream, const moe_trace* trace);

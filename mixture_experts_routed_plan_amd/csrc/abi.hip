@@ -134,9 +134,15 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
   }
   Tracer tr{trace, stream, 0};
   MOE_TRY(tr.mark());
-  MOE_TRY(launch_permute(*s, p.pos, x, xg, stream));
-  MOE_TRY(tr.mark());
-  MOE_TRY(launch_fprop_w13(*s, p, xg, w13, h13, a, stream));
+  if (fused_permute(*s)) {
+    // no xg: the gate/up GEMM reads each routed row's token row of x (the permute stage is empty)
+    MOE_TRY(tr.mark());
+    MOE_TRY(launch_fprop_w13(*s, p, x, w13, h13, a, stream, true));
+  } else {
+    MOE_TRY(launch_permute(*s, p.pos, x, xg, stream));
+    MOE_TRY(tr.mark());
+    MOE_TRY(launch_fprop_w13(*s, p, xg, w13, h13, a, stream));
+  }
   MOE_TRY(tr.mark());
   MOE_TRY(launch_fprop_w2(*s, p, a, w2, y, stream));
   MOE_TRY(tr.mark());

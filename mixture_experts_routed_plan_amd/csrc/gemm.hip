@@ -81,6 +81,9 @@ struct GemmArgs {
   const int2* mtiles;          // SCHED_ROWS: (expert, first row) per row tile
   const int32_t* mtile_count;  // SCHED_ROWS: number of row tiles (device)
   const int32_t* lpt;          // SCHED_KSEG: experts by decreasing row count
+  // P rows gathered from token rows (fused permute): P row r is row src[r] / gather_k of P
+  const int32_t* gather_src;   // null: P rows are the routed rows themselves
+  int gather_k;
 };
 
 // LDS tile layout: [rows][BK] bf16, each row BK/8 chunks of 16 bytes; logical chunk c of row r
@@ -291,11 +294,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   if constexpr (P_KC) {
     const int r0 = t.r0, rl = t.r_lim;
     const int64_t ldb = g.ldp * 2;
-    pd.init(g.P + (int64_t)r0 * g.ldp, [&](int row) -> uint32_t {
-      int r = r0 + row;
-      if (r > rl - 1) r = rl - 1;
-      return (uint32_t)((int64_t)(r - r0) * ldb);
-    });
+    if (g.gather_src) {
+      // fused permute (Dist-MoE "Understand the execution model": routing metadata drives the
+      // expert GEMMs; MoonEP FAQ: tokens go straight to their expert-grouped positions): the
+      // copies read each routed row's token row of x; offsets from the base of x (the host
+      // checks that x spans less than 4 GiB)
+      const int32_t* src = g.gather_src;
+      const int kk = g.gather_k;
+      pd.init(g.P, [&](int row) -> uint32_t {
+        int r = r0 + row;
+        if (r > rl - 1) r = rl - 1;
+        return (uint32_t)((int64_t)(src[r] / kk) * ldb);
+      });
+    } else {
+      pd.init(g.P + (int64_t)r0 * g.ldp, [&](int row) -> uint32_t {
+        int r = r0 + row;
+        if (r > rl - 1) r = rl - 1;
+        return (uint32_t)((int64_t)(r - r0) * ldb);
+      });
+    }
   } else {
     pm.init(g.P + (int64_t)t.kbeg * g.ldp + t.r0, g.ldp, 0, t.r_lim - t.r0);
   }
@@ -740,9 +757,14 @@ int rows_grid(const moe_shape& s, int bm, int ntn) {
 }  // namespace
 
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
-                            const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st) {
+                            const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,
+                            bool gather) {
   GemmArgs g = rows_args(s, p, kBM);
   g.P = xg; g.ldp = s.D;
+  if (gather) {  // xg is x: P rows come from the routed rows' tokens
+    g.gather_src = p.src;
+    g.gather_k = (int)s.K;
+  }
   g.Q = w13; g.ldq = s.D; g.q_estride = 2 * s.F * s.D;
   g.C = h13; g.ldc = 2 * s.F;
   g.C2 = a; g.ldc2 = s.F;

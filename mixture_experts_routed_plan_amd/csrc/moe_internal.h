@@ -77,6 +77,11 @@ inline SavedLayout saved_layout(const moe_shape& s) {
   return L;
 }
 
+// the forward without saving gathers token rows inside the gate/up GEMM when x spans < 4 GiB
+inline bool fused_permute(const moe_shape& s) {
+  return !(s.flags & MOE_SAVE_FOR_BACKWARD) && (uint64_t)s.T * (uint64_t)s.D * 2 < (1ull << 32);
+}
+
 // Workspace: the forward without saving keeps xg, a, y here (with MOE_RECOMPUTE only a); the
 // backward keeps dy (later reused for dxg, once dy is dead) and dh13; with MOE_RECOMPUTE also the
 // recomputed a (a_re), and the recomputed h13 sits where dh13 goes (the SwiGLU-derivative GEMM
@@ -91,7 +96,7 @@ inline WorkLayout work_layout(const moe_shape& s) {
   WorkLayout L{};
   const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
   L.xg = 0;
-  L.a = align_up(2 * N * D, 256);
+  L.a = fused_permute(s) ? 0 : align_up(2 * N * D, 256);  // no xg when the permute is fused
   L.y = L.a + align_up(2 * N * F, 256);
   L.fwd_total = L.y + align_up(2 * N * D, 256);
   L.dy = 0;
@@ -172,8 +177,11 @@ hipError_t launch_route(const moe_shape& s, const moe_router& r, const float* lo
                         float* weights, hipStream_t st);
 
 // grouped GEMMs
+// gather: xg is x[T,D] and the P rows are gathered through the plan's src (fused permute)
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
-                            const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st);
+                            const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,
+                            bool gather = false);
+
 hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
                            const uint16_t* w2, uint16_t* y, hipStream_t st);
 hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,

@@ -288,3 +288,20 @@ def test_large_sampled_weight_grads(name):
         assert_close("dw13", dv.bits_to_f64(dw13[e][jd[:, 0], jd[:, 1]]), v13)
         assert_close("dw2", dv.bits_to_f64(dw2[e][df[:, 0], df[:, 1]]), v2)
     log("[%s] oracle weight-grad entries: %.1fs" % (name, time.time() - t0))
+
+
+@pytest.mark.parametrize("name", ["fine_grained", "large_hidden"])
+def test_large_forward_without_save_sampled(name):
+    """Forward without saving (the permute fused into the gate/up GEMM, xg never written) at the
+    two forward-only workloads: out on 256 sampled tokens against the oracle, and every element of
+    out bitwise equal to the saving forward (which runs the separate permute)."""
+    _, dv = _lib()
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, with_dout=False, router=oracle.route)
+    ls, _ = run(inp, backward=False, save=True)
+    ln, _ = run(inp, backward=False, save=False)
+    np.testing.assert_array_equal(dv.to_host_bits(ln.out), dv.to_host_bits(ls.out))
+    toks = W.sample_tokens(w.T, 256, seed=1)
+    ref = oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks)
+    log("\n[%s] forward without saving" % name)
+    assert_close("out", dv.bits_to_f64(dv.to_host_bits(ln.out))[toks], ref["out"])
