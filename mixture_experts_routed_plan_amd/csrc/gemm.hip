@@ -49,8 +49,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;  // k per LDS stage
-constexpr int kEpWaveElems = 8704;  // per-wavefront epilogue staging area (bf16 elements)
-constexpr int kThreads = 256;
+// Wavefronts per workgroup: 8, two per SIMD, each owning 64 x 128 of the 256 x 256 tile (128
+// accumulator registers), so that while one wavefront of a SIMD waits (for LDS data, a copy, the
+// barrier) the other can issue MFMAs.
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kEpWaveElems = 65536 / kWaves;  // per-wavefront epilogue staging area (bf16 elements)
 constexpr int kGroupRows = 8;
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
@@ -187,7 +191,7 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
 // base plus a 32-bit byte offset per lane and block.
 template <int R>
 struct DmaTile {
-  static constexpr int NB = R / 32;  // blocks per wavefront = copy actions per stage
+  static constexpr int NB = R / 8 / kWaves;  // blocks per wavefront = copy actions per stage
   const char* base;                  // uniform
   uint32_t off[NB];                  // per lane, bytes from base (k = 0)
 
@@ -220,7 +224,7 @@ struct DmaTile {
 // zeroed in the P fragments (mask_tail in the kernel), so every product past kend is 0.
 template <int R>
 struct MnTile {
-  static constexpr int NB = 64 / 2 / 4;  // 1 KiB blocks per wavefront (8)
+  static constexpr int NB = 64 / 2 / kWaves;  // 1 KiB blocks per wavefront
   static_assert(R == 256, "MN tiles are 256 wide");
   const char* base;   // uniform: element (k = kbeg, idx = 0 of the tile's idx range)
   int64_t ldb;        // bytes between k rows
@@ -274,7 +278,9 @@ __device__ __forceinline__ v4i16 read_mn_half(const uint16_t* tile, int idx0, in
 
 template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI, int OUT = OUT_BF16>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int WR = kWaves / 2;  // wavefront rows (P) x 2 wavefront columns (Q)
+  constexpr int WM = BM / WR, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int MPK = FN * FM;  // MFMAs per k sub-step and wavefront
   static_assert(BM == 256 && BN == 256, "the interleaved schedule below assumes 256x256 tiles");
   constexpr int BK = kBK;
   constexpr bool MASK_K = SCHED == SCHED_KSEG;
@@ -285,7 +291,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = wave % WR, wc = wave / WR;
   const int klen = t.kend - t.kbeg;
 
   // operand P (rows of the output)
@@ -358,14 +364,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   auto addrP = [&](int b) { return lds0 + (uint32_t)(b * (BM + BN) * BK * 2); };
   auto addrQ = [&](int b) { return lds0 + (uint32_t)((b * (BM + BN) * BK + BM * BK) * 2); };
 
-  // copy of one stage: 8 DMA blocks per operand and wavefront
-  static_assert(DmaTile<BM>::NB == 8 && MnTile<BM>::NB == 8, "8 copies per operand");
+  // copy of one stage: NBO DMA blocks per operand and wavefront
+  constexpr int NBO = DmaTile<BM>::NB, NC = 2 * NBO;
+  static_assert(DmaTile<BM>::NB == MnTile<BM>::NB && DmaTile<BN>::NB == NBO, "copies per operand");
   auto copy_issue = [&](int b, int kt, int n) {
     const int k0 = kt * BK;  // relative to kbeg
-    if (n < 8) {
+    if (n < NBO) {
       if constexpr (P_KC) pd.issue(addrP(b), t.kbeg + k0, n); else pm.issue(addrP(b), k0, klen, n);
     } else {
-      if constexpr (Q_KC) qd.issue(addrQ(b), t.kbeg + k0, n - 8); else qm.issue(addrQ(b), k0, klen, n - 8);
+      if constexpr (Q_KC) qd.issue(addrQ(b), t.kbeg + k0, n - NBO); else qm.issue(addrQ(b), k0, klen, n - NBO);
     }
   };
 
@@ -413,15 +420,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
   };
 
-  // Schedule of one stage (64 MFMAs: m = 0..15 in each of the 4 k sub-steps ks): with one
-  // wavefront per SIMD the matrix unit only stays busy if every other instruction slips in
-  // between MFMAs, so after MFMA (ks, m):
-  //   ks < 3:              the LDS read operations of sub-step ks+1, spread over the 16 slots
-  //   ks < 2, m odd:       one DMA copy of the next stage (into the other buffer)
-  //   before (3, 12):      wait for this wave's copies, barrier: every wave's copies of the next
+  // Schedule of one stage (MPK MFMAs m in each of the 4 k sub-steps ks): every other instruction
+  // slips in between MFMAs, so after MFMA (ks, m):
+  //   ks < 3:              the LDS read operations of sub-step ks+1, spread over the MPK slots
+  //   ks < 2:              the NC DMA copies of the next stage (into the other buffer), spread
+  //                        over the 2 MPK slots of sub-steps 0 and 1
+  //   before (3, B0):      wait for this wave's copies, barrier: every wave's copies of the next
   //                        stage have landed, and this buffer is no longer read after this point
-  //   ks = 3, m >= 12:     the read operations of sub-step 0 of the next stage
+  //   ks = 3, m >= B0:     the read operations of sub-step 0 of the next stage
   // The buffer written during stage s was last read before the barrier of stage s-1.
+  constexpr int B0 = MPK * 3 / 4;
   // this wavefront's 32-row blocks (jlim of FM) and 32-column blocks (ilim of FN; for the SwiGLU
   // forward per gate/up half) that hold any output: the products of the others (the ragged last
   // row tile of an expert, a column tail) are skipped
@@ -448,24 +456,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int ks = 0; ks < 4; ++ks) {
       mask_tail(kt, ks);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        if (ks == 3 && m == 12) {
+      for (int m = 0; m < MPK; ++m) {
+        if (ks == 3 && m == B0) {
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (!MASKED || block_on(m >> 2, m & 3))
-          acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              qa[ks & 1][m >> 2], pb[ks & 1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+        if (!MASKED || block_on(m / FM, m % FM))
+          acc[m / FM][m % FM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              qa[ks & 1][m / FM], pb[ks & 1][m % FM], acc[m / FM][m % FM], 0, 0, 0);
         if (ks < 3) {
 #pragma unroll
-          for (int n = (m * NR) / 16; n < ((m + 1) * NR) / 16; ++n) read_op(cur, ks + 1, n);
+          for (int n = (m * NR) / MPK; n < ((m + 1) * NR) / MPK; ++n) read_op(cur, ks + 1, n);
         }
         if (more) {
-          if (ks < 2 && (m & 1) == 1) copy_issue(nxt, kt + 1, ks * 8 + (m >> 1));
-          if (ks == 3 && m >= 12) {
+          if (ks < 2) {
+            const int sl = ks * MPK + m;
 #pragma unroll
-            for (int n = ((m - 12) * NR) / 4; n < ((m - 11) * NR) / 4; ++n) read_op(nxt, 0, n);
+            for (int n = (sl * NC) / (2 * MPK); n < ((sl + 1) * NC) / (2 * MPK); ++n)
+              copy_issue(nxt, kt + 1, n);
+          }
+          if (ks == 3 && m >= B0) {
+#pragma unroll
+            for (int n = ((m - B0) * NR) / (MPK - B0); n < ((m - B0 + 1) * NR) / (MPK - B0); ++n)
+              read_op(nxt, 0, n);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -474,7 +488,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   };
   if (nk > 0) {
 #pragma unroll
-    for (int n = 0; n < 16; ++n) copy_issue(0, 0, n);
+    for (int n = 0; n < NC; ++n) copy_issue(0, 0, n);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -519,18 +533,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
   };
   if constexpr (EPI == EPI_STORE && OUT != OUT_BF16) {
-    // fp32 staging ([32][WN + 4] floats per wavefront), then per 8 consecutive outputs of a row:
-    // optionally the existing values added in fp32, then one rounding (bf16) or none (fp32)
-    constexpr int PW = WN + 4;
+    // fp32 staging ([32][W + 4] floats per wavefront, per 64-column half), then per 8 consecutive
+    // outputs of a row: optionally the existing values added in fp32, then one rounding (bf16)
+    // or none (fp32)
+    constexpr int W = WN / 2, PW = W + 4;
     static_assert(32 * PW * 4 <= kEpWaveElems * 2, "fp32 staging area");
     float* epf = (float*)ep;
     const int64_t cofs = (int64_t)t.e * g.c_estride;
-    constexpr int per_row = WN / 8, rows_per_pass = 64 / per_row;
+    constexpr int per_row = W / 8, rows_per_pass = 64 / per_row;
     constexpr int NP = 32 / rows_per_pass;  // flush passes per 32-row block
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
+    for (int hj = 0; hj < 2 * FM; ++hj) {
+      const int hlf = hj & 1, j = hj >> 1;
       if (j >= jlim) break;
-      const int row0 = t.r0 + wr * WM + j * 32, col0 = t.n0 + wc * WN;
+      const int row0 = t.r0 + wr * WM + j * 32, col0 = t.n0 + wc * WN + hlf * W;
       // the existing values this lane adds to, loaded before the staging so that their latency
       // overlaps it
       uint4 oldb[OUT == OUT_BF16_ACC ? NP : 1];
@@ -551,12 +567,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
+      for (int ii = 0; ii < FN / 2; ++ii)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          *(float4*)(epf + rl * PW + i * 32 + gq * 8 + cq) =
+        for (int gq = 0; gq < 4; ++gq) {
+          const int i = hlf * (FN / 2) + ii;
+          *(float4*)(epf + rl * PW + ii * 32 + gq * 8 + cq) =
               make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
                           acc[i][j][4 * gq + 3]);
+        }
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
         const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
@@ -640,54 +658,61 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
     }
   } else {  // EPI_SWIGLU_BWD: acc = da over columns f; g, u come from the saved h13
-    constexpr int PW = WN + 4;
+    // two passes over 64-column halves of the wavefront's 128 columns; per 32-row block the g and
+    // u row segments are loaded coalesced into [32][68] areas, replaced in place by dg and du,
+    // and stored
+    constexpr int W = WN / 2, PW = W + 4, per_row = W / 8, rows_per_pass = 64 / per_row;
+    static_assert(2 * 32 * PW <= kEpWaveElems, "g/u staging area");
     uint16_t* e1 = ep;             // g, then dg
     uint16_t* e2 = ep + 32 * PW;   // u, then du
-    const int f0w = t.n0 + wc * WN;
-    constexpr int per_row = WN / 8, rows_per_pass = 64 / per_row;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      if (j >= jlim) break;
-      const int row0 = t.r0 + wr * WM + j * 32;
-      // coalesced loads of the g and u row segments (rows past the segment clamped)
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int f0w = t.n0 + wc * WN + hlf * W;
 #pragma unroll
-      for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
-        const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
-        int r = row0 + row;
-        if (r > t.r_lim - 1) r = t.r_lim - 1;
-        int c = f0w + ch * 8;
-        if (c > g.F - 8) c = g.F - 8;
-        const uint16_t* hrow = g.H + (int64_t)r * g.ldh + c;
-        const uint4 gv = *(const uint4*)hrow, uv = *(const uint4*)(hrow + g.F);
-        uint16_t* d1 = e1 + row * PW + ch * 8;
-        uint16_t* d2 = e2 + row * PW + ch * 8;
-        *(uint2*)d1 = make_uint2(gv.x, gv.y);
-        *(uint2*)(d1 + 4) = make_uint2(gv.z, gv.w);
-        *(uint2*)d2 = make_uint2(uv.x, uv.y);
-        *(uint2*)(d2 + 4) = make_uint2(uv.z, uv.w);
-      }
+      for (int j = 0; j < FM; ++j) {
+        if (j >= jlim) break;
+        const int row0 = t.r0 + wr * WM + j * 32;
+        // coalesced loads of the g and u row segments (rows past the segment clamped)
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int o = rl * PW + i * 32 + gq * 8 + cq;
-          const uint2 gh = *(const uint2*)(e1 + o), uh = *(const uint2*)(e2 + o);
-          const uint32_t gw[4] = {gh.x & 0xffffu, gh.x >> 16, gh.y & 0xffffu, gh.y >> 16};
-          const uint32_t uw[4] = {uh.x & 0xffffu, uh.x >> 16, uh.y & 0xffffu, uh.y >> 16};
-          float dg[4], du[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gv = bf16_to_f32(gw[q]), uv = bf16_to_f32(uw[q]);
-            const float da = acc[i][j][4 * gq + q];
-            const float sg = sigmoid_f32(gv);
-            dg[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
-            du[q] = da * gv * sg;
-          }
-          *(uint2*)(e1 + o) = make_uint2(pk2(dg[0], dg[1]), pk2(dg[2], dg[3]));
-          *(uint2*)(e2 + o) = make_uint2(pk2(du[0], du[1]), pk2(du[2], du[3]));
+        for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+          const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
+          int r = row0 + row;
+          if (r > t.r_lim - 1) r = t.r_lim - 1;
+          int c = f0w + ch * 8;
+          if (c > g.F - 8) c = g.F - 8;
+          const uint16_t* hrow = g.H + (int64_t)r * g.ldh + c;
+          const uint4 gv = *(const uint4*)hrow, uv = *(const uint4*)(hrow + g.F);
+          uint16_t* d1 = e1 + row * PW + ch * 8;
+          uint16_t* d2 = e2 + row * PW + ch * 8;
+          *(uint2*)d1 = make_uint2(gv.x, gv.y);
+          *(uint2*)(d1 + 4) = make_uint2(gv.z, gv.w);
+          *(uint2*)d2 = make_uint2(uv.x, uv.y);
+          *(uint2*)(d2 + 4) = make_uint2(uv.z, uv.w);
         }
-      flush(e1, WN, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
-      flush(e2, WN, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
+#pragma unroll
+        for (int ii = 0; ii < FN / 2; ++ii)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int i = hlf * (FN / 2) + ii;
+            const int o = rl * PW + ii * 32 + gq * 8 + cq;
+            const uint2 gh = *(const uint2*)(e1 + o), uh = *(const uint2*)(e2 + o);
+            const uint32_t gw[4] = {gh.x & 0xffffu, gh.x >> 16, gh.y & 0xffffu, gh.y >> 16};
+            const uint32_t uw[4] = {uh.x & 0xffffu, uh.x >> 16, uh.y & 0xffffu, uh.y >> 16};
+            float dg[4], du[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float gv = bf16_to_f32(gw[q]), uv = bf16_to_f32(uw[q]);
+              const float da = acc[i][j][4 * gq + q];
+              const float sg = sigmoid_f32(gv);
+              dg[q] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+              du[q] = da * gv * sg;
+            }
+            *(uint2*)(e1 + o) = make_uint2(pk2(dg[0], dg[1]), pk2(dg[2], dg[3]));
+            *(uint2*)(e2 + o) = make_uint2(pk2(du[0], du[1]), pk2(du[2], du[3]));
+          }
+        flush(e1, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
+        flush(e2, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
+      }
     }
   }
 }
@@ -695,7 +720,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 constexpr int kBM = 256, kBN = 256;
 
 #define MOE_GEMM_KERNEL(name, P_KC, Q_KC, SCHED, EPI)                                          \
-  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void name( \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void name( \
       GemmArgs g) {                                                                            \
     gemm_body<kBM, kBN, P_KC, Q_KC, SCHED, EPI>(g);                                            \
   }
@@ -709,7 +734,7 @@ MOE_GEMM_KERNEL(moe_wgrad_w13, false, false, SCHED_KSEG, EPI_STORE)
 
 // weight gradients accumulated into existing storage, or kept in fp32
 #define MOE_WGRAD_KERNEL(name, OUT)                                                             \
-  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void name( \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void name( \
       GemmArgs g) {                                                                            \
     gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(g);                          \
   }

@@ -124,7 +124,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// logistic sigmoid in fp32: hardware exp2 (v_exp_f32) and reciprocal (v_rcp_f32, 1 ulp) instead
+// of the IEEE division sequence; the result feeds a bf16 rounding
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ------------------------------------------------------------------------------------------
 // launchers (return hipSuccess or the launch error)
