@@ -423,8 +423,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // Schedule of one stage (MPK MFMAs m in each of the 4 k sub-steps ks): every other instruction
   // slips in between MFMAs, so after MFMA (ks, m):
   //   ks < 3:              the LDS read operations of sub-step ks+1, spread over the MPK slots
-  //   ks < 2:              the NC DMA copies of the next stage (into the other buffer), spread
-  //                        over the 2 MPK slots of sub-steps 0 and 1
+  //   ks = 0:              the NC DMA copies of the next stage (into the other buffer), spread
+  //                        over the MPK slots of sub-step 0 (the earliest issue gives them the
+  //                        most time to land before the barrier)
   //   before (3, B0):      wait for this wave's copies, barrier: every wave's copies of the next
   //                        stage have landed, and this buffer is no longer read after this point
   //   ks = 3, m >= B0:     the read operations of sub-step 0 of the next stage
@@ -470,11 +471,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           for (int n = (m * NR) / MPK; n < ((m + 1) * NR) / MPK; ++n) read_op(cur, ks + 1, n);
         }
         if (more) {
-          if (ks < 2) {
-            const int sl = ks * MPK + m;
+          if (ks == 0) {
 #pragma unroll
-            for (int n = (sl * NC) / (2 * MPK); n < ((sl + 1) * NC) / (2 * MPK); ++n)
-              copy_issue(nxt, kt + 1, n);
+            for (int n = (m * NC) / MPK; n < ((m + 1) * NC) / MPK; ++n) copy_issue(nxt, kt + 1, n);
           }
           if (ks == 3 && m >= B0) {
 #pragma unroll
