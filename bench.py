@@ -245,12 +245,69 @@ def profiled_traffic(workload, kernel_short):
     return None
 
 
+def M_lib():
+    import mixture_experts_routed_plan_amd as M
+    return M
+
+
+def extras(args, w, dv, M, x, scores, w13, w2, ids, stream, hip):
+    """Forward-only timing (no saving: the permute is fused into the gate/up GEMM) and the
+    router on this workload's token and expert counts."""
+    import torch
+    fl = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=False, alloc_grads=False)
+    fl.plan(ids, stream)
+    for _ in range(2):
+        fl.forward(x, scores, w13, w2, stream)
+    f0, f1 = hip.create(), hip.create()
+    torch.cuda.synchronize()
+    hip.record(f0, stream)
+    for _ in range(args.steps):
+        fl.forward(x, scores, w13, w2, stream)
+    hip.record(f1, stream)
+    torch.cuda.synchronize()
+    f_ms = hip.ms(f0, f1) / args.steps
+    forward_only = {"ms": round(f_ms, 4),
+                    "tflops": round(6 * w.N * w.D * w.F / (f_ms / 1e3) / 1e12, 1),
+                    "tokens_per_s": round(w.T / (f_ms / 1e3), 1),
+                    "config": "forward without saving (permute fused into the gate/up GEMM), "
+                              "plan excluded"}
+    del fl
+
+    # the router on this workload's token and expert counts (N(0,1) logits, softmax top-K,
+    # renormalised): HBM-bound on logits read plus ids and weights written
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    logits = torch.randn(w.T, w.E, device="cuda", generator=g)
+    r_ids = torch.empty(w.T, w.K, dtype=torch.int64, device="cuda")
+    r_sc = torch.empty(w.T, w.K, dtype=torch.float32, device="cuda")
+    r_shape = M.make_shape(w.T, w.D, w.F, w.E, w.K)
+    r_cfg = M.make_router()
+    M.check(M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream), "moe_route")
+    r0, r1 = hip.create(), hip.create()
+    torch.cuda.synchronize()
+    hip.record(r0, stream)
+    for _ in range(20):
+        M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream)
+    hip.record(r1, stream)
+    torch.cuda.synchronize()
+    r_ms = hip.ms(r0, r1) / 20
+    r_bytes = 4 * w.T * w.E + 12 * w.T * w.K
+    router = {"ms": round(r_ms, 4), "gbs": round(r_bytes / r_ms / 1e6, 1),
+              "frac_peak": round(r_bytes / r_ms / 1e6 / PEAK_HBM_GBS, 4),
+              "config": "softmax top-%d of %d, renormalised, %d tokens" % (w.K, w.E, w.T)}
+
+    return forward_only, router
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large_hidden")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="time only the fwd+bwd step (no forward-only and router lines; for "
+                         "profiling runs, so that each kernel's statistics cover the step alone)")
     ap.add_argument("--recompute", action="store_true",
                     help="save only xg and y; the backward recomputes h13 and a")
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "bf16-accumulate", "f32", "f32-accumulate"],
@@ -389,49 +446,9 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
-    # forward only (inference; no saving, so the permute is fused into the gate/up GEMM)
-    fl = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=False, alloc_grads=False)
-    fl.plan(ids, stream)
-    for _ in range(2):
-        fl.forward(x, scores, w13, w2, stream)
-    f0, f1 = hip.create(), hip.create()
-    torch.cuda.synchronize()
-    hip.record(f0, stream)
-    for _ in range(args.steps):
-        fl.forward(x, scores, w13, w2, stream)
-    hip.record(f1, stream)
-    torch.cuda.synchronize()
-    f_ms = hip.ms(f0, f1) / args.steps
-    forward_only = {"ms": round(f_ms, 4),
-                    "tflops": round(6 * w.N * w.D * w.F / (f_ms / 1e3) / 1e12, 1),
-                    "tokens_per_s": round(w.T / (f_ms / 1e3), 1),
-                    "config": "forward without saving (permute fused into the gate/up GEMM), "
-                              "plan excluded"}
-    del fl
-
-    # the router on this workload's token and expert counts (N(0,1) logits, softmax top-K,
-    # renormalised): HBM-bound on logits read plus ids and weights written
-    import mixture_experts_routed_plan_amd as M
-    g = torch.Generator(device="cuda")
-    g.manual_seed(0)
-    logits = torch.randn(w.T, w.E, device="cuda", generator=g)
-    r_ids = torch.empty(w.T, w.K, dtype=torch.int64, device="cuda")
-    r_sc = torch.empty(w.T, w.K, dtype=torch.float32, device="cuda")
-    r_shape = M.make_shape(w.T, w.D, w.F, w.E, w.K)
-    r_cfg = M.make_router()
-    M.check(M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream), "moe_route")
-    r0, r1 = hip.create(), hip.create()
-    torch.cuda.synchronize()
-    hip.record(r0, stream)
-    for _ in range(20):
-        M.moe_route(r_shape, r_cfg, logits, r_ids, r_sc, stream)
-    hip.record(r1, stream)
-    torch.cuda.synchronize()
-    r_ms = hip.ms(r0, r1) / 20
-    r_bytes = 4 * w.T * w.E + 12 * w.T * w.K
-    router = {"ms": round(r_ms, 4), "gbs": round(r_bytes / r_ms / 1e6, 1),
-              "frac_peak": round(r_bytes / r_ms / 1e6 / PEAK_HBM_GBS, 4),
-              "config": "softmax top-%d of %d, renormalised, %d tokens" % (w.K, w.E, w.T)}
+    forward_only = router = None
+    if not args.skip_extras:
+        forward_only, router = extras(args, w, dv, M_lib(), x, scores, w13, w2, ids, stream, hip)
 
     flops = 18 * w.N * w.D * w.F
     res = {
