@@ -291,7 +291,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches
-  const int wr = wave % WR, wc = wave / WR;
+  // wavefront w runs on SIMD w % 4, so SIMD s hosts wavefronts s and s + 4: with wr = w / 2 they
+  // own row groups of the two different 128-row halves of the tile, and a tile whose last rows are
+  // past the end of the expert's segment (the ragged last tile) still keeps every SIMD busy
+  const int wr = wave / 2, wc = wave % 2;
   const int klen = t.kend - t.kbeg;
 
   // operand P (rows of the output)
