@@ -305,3 +305,31 @@ def test_large_forward_without_save_sampled(name):
     ref = oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks)
     log("\n[%s] forward without saving" % name)
     assert_close("out", dv.bits_to_f64(dv.to_host_bits(ln.out))[toks], ref["out"])
+
+
+# ------------------------------------------------------------------------------------------------
+# degenerate shapes, every element
+
+DEGENERATE = [
+    # (T, D, F, E, K, routing, seed): one token, one expert, one slot; more experts than slots
+    # (most experts empty); K = E with every expert in every token; a single 64-wide hidden and
+    # intermediate; row tiles of exactly 256 rows; one ragged row after a full tile; the largest
+    # E and K
+    (1, 64, 64, 1, 1, "even", 11),
+    (3, 128, 64, 16, 2, "uniform_distinct", 12),
+    (40, 192, 128, 4, 4, "uniform_distinct", 13),
+    (64, 64, 64, 2, 1, "even", 14),
+    (512, 128, 192, 2, 1, "even", 15),
+    (257, 64, 128, 1, 1, "even", 16),
+    (64, 64, 64, 1024, 64, "uniform_distinct", 17),  # the largest E and K: 1024 tiny segments
+]
+
+
+@pytest.mark.parametrize("T,D,F,E,K,routing,seed", DEGENERATE)
+def test_layer_parity_degenerate_shapes(T, D, F, E, K, routing, seed):
+    w = W.Workload("degenerate", T=T, D=D, F=F, E=E, K=K, routing=routing, backward=True,
+                   seed=seed)
+    inp = W.make_inputs(w, router=oracle.route)
+    log("\n[degenerate] T=%d D=%d F=%d E=%d K=%d %s" % (T, D, F, E, K, routing))
+    layer, _ = run(inp)
+    _full_check(inp, layer)
