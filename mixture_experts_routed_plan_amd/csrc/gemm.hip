@@ -291,9 +291,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches
-  // wavefront w runs on SIMD w % 4, so SIMD s hosts wavefronts s and s + 4: with wr = w / 2 they
-  // own row groups of the two different 128-row halves of the tile, and a tile whose last rows are
-  // past the end of the expert's segment (the ragged last tile) still keeps every SIMD busy
+  // Wavefront row group wr owns the interleaved 32-row blocks wr, wr + WR, ... of the tile, and
+  // wavefront w runs on SIMD w % 4, so SIMD s hosts wavefronts s and s + 4 (row groups s/2 and
+  // s/2 + 2): the first rows of a tile spread over all four SIMDs, and a partly filled tile (the
+  // ragged last row tile of an expert) runs in proportion to its rows
   const int wr = wave / 2, wc = wave % 2;
   const int klen = t.kend - t.kbeg;
 
@@ -398,11 +399,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     } else {
       const int m = n - RQ;
       if constexpr (P_KC) {
-        const int row = wr * WM + m * 32 + (lane & 31);
+        const int row = (wr + WR * m) * 32 + (lane & 31);
         const int ch = ks * 2 + (lane >> 5);
         pb[ks & 1][m] = *(const bf16x8*)(bufP(b) + row * BK + swz<BK>(row, ch) * 8);
       } else {
-        const v4i16 h = read_mn_half(bufP(b), wr * WM + (m >> 1) * 32, ks, m & 1);
+        const v4i16 h = read_mn_half(bufP(b), (wr + WR * (m >> 1)) * 32, ks, m & 1);
         v4i16* dst = (v4i16*)&pb[ks & 1][m >> 1];
         dst[m & 1] = h;
       }
@@ -437,8 +438,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // this wavefront's 32-row blocks (jlim of FM) and 32-column blocks (ilim of FN; for the SwiGLU
   // forward per gate/up half) that hold any output: the products of the others (the ragged last
   // row tile of an expert, a column tail) are skipped
-  const int rows_left = t.r_lim - (t.r0 + wr * WM);
-  const int jlim = rows_left <= 0 ? 0 : (rows_left >= WM ? FM : (rows_left + 31) / 32);
+  const int tile_rows = t.r_lim - t.r0;
+  const int nblk = tile_rows >= BM ? BM / 32 : (tile_rows + 31) / 32;  // 32-row blocks with rows
+  const int jlim = nblk <= wr ? 0 : min(FM, (nblk - wr + WR - 1) / WR);
   int ilim;
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     const int cols_left = g.F - (t.n0 + wc * (WN / 2));
@@ -504,7 +506,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   // ---- epilogue ------------------------------------------------------------------------------
   // Lane (lane&31, lane>>5) of the wavefront holds, for MFMA block (i, j), output row
-  // j*32 + (lane&31) of the wavefront's 128 rows and the 4 consecutive columns
+  // (wr + WR*j)*32 + (lane&31) of the tile and the 4 consecutive columns
   // i*32 + 8*gq + 4*(lane>>5) + 0..3, gq = 0..3. Per 32-row block j the wavefront converts its
   // values to bf16 (v_cvt_pk_bf16_f32, round to nearest even), parks them in a private LDS area
   // with padded rows (the 8-byte writes of 32 rows land on distinct banks), reads them back as
@@ -548,7 +550,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int hj = 0; hj < 2 * FM; ++hj) {
       const int hlf = hj & 1, j = hj >> 1;
       if (j >= jlim) break;
-      const int row0 = t.r0 + wr * WM + j * 32, col0 = t.n0 + wc * WN + hlf * W;
+      const int row0 = t.r0 + (wr + WR * j) * 32, col0 = t.n0 + wc * WN + hlf * W;
       // the existing values this lane adds to, loaded before the staging so that their latency
       // overlaps it
       uint4 oldb[OUT == OUT_BF16_ACC ? NP : 1];
@@ -624,7 +626,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           *(uint2*)(ep + rl * PW + i * 32 + gq * 8 + cq) =
               make_uint2(pk2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
                          pk2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]));
-      flush(ep, WN, C, g.ldc, t.r0 + wr * WM + j * 32, t.r_lim, t.n0 + wc * WN, g.N_out);
+      flush(ep, WN, C, g.ldc, t.r0 + (wr + WR * j) * 32, t.r_lim, t.n0 + wc * WN, g.N_out);
     }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
     // the wavefront's 64 activation columns f0w .. f0w+63: a, g and u each through [32][68]
@@ -652,7 +654,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           *(uint2*)(eu + o) = make_uint2(pk2(uv[0], uv[1]), pk2(uv[2], uv[3]));
           *(uint2*)(ea + o) = make_uint2(pk2(av[0], av[1]), pk2(av[2], av[3]));
         }
-      const int row0 = t.r0 + wr * WM + j * 32;
+      const int row0 = t.r0 + (wr + WR * j) * 32;
       flush(ea, W, g.C2, g.ldc2, row0, t.r_lim, f0w, g.F);
       if (g.C) {
         flush(eg, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
@@ -673,7 +675,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         if (j >= jlim) break;
-        const int row0 = t.r0 + wr * WM + j * 32;
+        const int row0 = t.r0 + (wr + WR * j) * 32;
         // coalesced loads of the g and u row segments (rows past the segment clamped)
 #pragma unroll
         for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
