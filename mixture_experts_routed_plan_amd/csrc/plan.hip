@@ -82,13 +82,21 @@ __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int3
   const int tid = threadIdx.x;
 
   // chunk bases within each expert (exclusive scan over chunks, in place) and the counts
+  // (the counts of a batch of chunks are loaded before any of them is overwritten, so the loads
+  // of a batch are in flight together)
   int cnt = 0;
   if (tid < E) {
+    constexpr int kBatch = 16;
     int32_t* row = blkhist + (int64_t)tid * NB;
-    for (int b = 0; b < NB; ++b) {
-      const int v = row[b];
-      row[b] = cnt;
-      cnt += v;
+    for (int b0 = 0; b0 < NB; b0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) v[q] = b0 + q < NB ? row[b0 + q] : 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (b0 + q < NB) row[b0 + q] = cnt;
+        cnt += v[q];
+      }
     }
     counts[tid] = cnt;
   }
