@@ -148,6 +148,13 @@ def _short_kernel(name):
     return n.strip()
 
 
+def _family(name):
+    """Kernel name without its slot-count template argument (moe_combine<true, 8> ->
+    moe_combine<true>, moe_combine_bwd_dscores<8> -> moe_combine_bwd_dscores)."""
+    import re
+    return re.sub(r"<\d+>$", "", re.sub(r", \d+>$", ">", name))
+
+
 def _counter_means(path):
     import csv
     import collections
@@ -177,6 +184,8 @@ def summarize(prof_dir, out_path, workload, cmd):
         os.path.join(prof_dir, "probe_mib")) else 1024 * 1024
     f_fac = probe_kib / fetch[copy[0]]["FETCH_SIZE"]
     w_fac = probe_kib / write[copy[0]]["WRITE_SIZE"]
+    copy_t = [v for k, v in stats.items() if "copyBuffer" in k]
+    copy_tbs = (2 * probe_kib * 1024 / (copy_t[0][1] * 1e-6) / 1e12) if copy_t else None
     rows = []
     table = {}
     for k, (calls, avg, mn, mx) in sorted(stats.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
@@ -212,7 +221,11 @@ def summarize(prof_dir, out_path, workload, cmd):
         "1024`, runtime kernel `__amd_rocclr_copyBuffer`), which reads and writes exactly "
         "1048576 KiB. On it FETCH_SIZE reads %.0f KiB and WRITE_SIZE %.0f KiB, so HBM-side "
         "traffic = %.3f x FETCH_SIZE + %.3f x WRITE_SIZE (KiB per dispatch)."
-        % (fetch[copy[0]]["FETCH_SIZE"], write[copy[0]]["WRITE_SIZE"], f_fac, w_fac), "",
+        % (fetch[copy[0]]["FETCH_SIZE"], write[copy[0]]["WRITE_SIZE"], f_fac, w_fac)
+        + (" The copy itself took %.1f us in the kernel-trace run: %.2f TB/s of reads plus "
+           "writes (%.0f%% of the 8 TB/s HBM peak), the streaming rate the row kernels are "
+           "measured against." % (copy_t[0][1], copy_tbs, copy_tbs / 8 * 100) if copy_tbs else ""),
+        "",
         "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
         "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS). Counter runs serialize kernels, so their "
         "durations are not used; the times come from the kernel-trace run.", "",
@@ -239,9 +252,9 @@ def profiled_traffic(workload, kernel_short):
                 meta = json.loads(line)
                 if meta.get("workload") != workload or meta.get("source_digest") != source_digest():
                     continue
-                ent = meta["kernels"].get(kernel_short)
-                if ent and ent.get("traffic_bytes"):
-                    return ent["traffic_bytes"]
+                for k, ent in meta["kernels"].items():
+                    if _family(k) == kernel_short and ent.get("traffic_bytes"):
+                        return ent["traffic_bytes"]
     return None
 
 

@@ -63,11 +63,38 @@ class MoeError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (what or "moe", moe_status_str(status), status))
 
 
+def _hip_runtimes():
+    """Distinct HIP runtime libraries mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                path = line.split()[-1]
+                if os.path.basename(path).startswith("libamdhip64"):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return sorted(found)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("%s is not built; run `python -m mixture_experts_routed_plan_amd.build`"
                           % LIB_PATH)
+    # The library and torch must share one HIP runtime: torch's streams and allocations belong to
+    # the runtime torch loaded, and torch ships its own copy of the HIP and HSA runtimes. With
+    # torch imported first, the library's libamdhip64 dependency resolves to that copy; loading
+    # the library first would map a second runtime into the process, and its launches on torch's
+    # streams would fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (%s): import torch before "
+                          "any other library that links a HIP runtime" % ", ".join(runtimes))
     P, S, St = ctypes.c_void_p, ctypes.POINTER(moe_shape), ctypes.c_int
     Tr = ctypes.POINTER(moe_trace)
     sigs = {

@@ -33,13 +33,21 @@ __global__ __launch_bounds__(64) void moe_plan_hist(const IdT* __restrict__ ids,
   const int lane = threadIdx.x, b = blockIdx.x;
   for (int e = lane; e < E; e += 64) h[e] = 0;
   __syncthreads();
+  // every id of the chunk is loaded before the first count, so the loads are in flight together
+  constexpr int kPer = kPlanChunk / 64;
   const int lo = b * kPlanChunk, hi = min(N, lo + kPlanChunk);
+  int v[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = lo + lane + 64 * q;
+    v[q] = i < hi ? load_expert(ids, i, E) : -2;  // -2: past the end of the slots
+  }
   int bad = 0;
-  for (int i = lo + lane; i < hi; i += 64) {
-    const int v = load_expert(ids, i, E);
-    if (v >= 0)
-      atomicAdd(&h[v], 1);
-    else
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (v[q] >= 0)
+      atomicAdd(&h[v[q]], 1);
+    else if (v[q] == -1)
       ++bad;
   }
   __syncthreads();
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int3
   // of a batch are in flight together)
   int cnt = 0;
   if (tid < E) {
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 32;
     int32_t* row = blkhist + (int64_t)tid * NB;
     for (int b0 = 0; b0 < NB; b0 += kBatch) {
       int v[kBatch];
@@ -136,12 +144,13 @@ __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int3
   // rows past the last routed row have no source slot
   for (int r = nvalid + tid; r < N; r += 1024) src[r] = -1;
 
-  if (tid == 0) {
-    int bad = 0;
-    for (int b = 0; b < NB; ++b) bad += blkbad[b];
-    status[0] = bad;
+  // out-of-range total: per-thread partial sums over the chunks, then one scan
+  int badp = 0;
+  for (int b = tid; b < NB; b += 1024) badp += blkbad[b];
+  const int bad = block_scan_1024(badp, wsum);
+  if (tid == 1023) status[0] = bad;
+  if (tid == 0)
     for (int w = 1 + kNumTileSizes; w < kStatusWords; ++w) status[w] = 0;
-  }
 }
 
 template <typename IdT>
@@ -153,14 +162,25 @@ __global__ __launch_bounds__(64) void moe_plan_scatter(const IdT* __restrict__ i
                                                      int32_t* __restrict__ src) {
   __shared__ int32_t base[MOE_MAX_EXPERTS];
   const int lane = threadIdx.x, b = blockIdx.x;
+  // the chunk's ids are loaded up front, their loads in flight together with the bases'
+  constexpr int kPer = kPlanChunk / 64;
+  const int lo = b * kPlanChunk, hi = min(N, lo + kPlanChunk);
+  int vv[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = lo + lane + 64 * q;
+    vv[q] = i < hi ? load_expert(ids, i, E) : -1;
+  }
   for (int e = lane; e < E; e += 64) base[e] = offsets[e] + blkhist[(int64_t)e * NB + b];
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int lo = b * kPlanChunk, hi = min(N, lo + kPlanChunk);
-  for (int i0 = lo; i0 < hi; i0 += 64) {
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i0 = lo + 64 * q;
+    if (i0 >= hi) break;  // uniform
     const int i = i0 + lane;
     const bool in = i < hi;
-    const int v = in ? load_expert(ids, i, E) : -1;
+    const int v = vv[q];
     const bool ok = v >= 0;
     // lanes holding the same expert id: agree on every bit of the id
     uint64_t peers = __ballot(ok);

@@ -148,3 +148,13 @@ def test_importing_without_the_library_fails_loudly(tmp_path):
     (pkg / "__init__.py").write_text(src)
     r = subprocess.run(["python", "-c", code], capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_one_hip_runtime_when_imported_before_torch():
+    """torch ships its own HIP runtime; the binding loads the library after importing torch, so
+    the process maps one runtime even when the package is imported first (a second runtime would
+    make launches on torch's streams fail)."""
+    code = ("import mixture_experts_routed_plan_amd as M\nimport torch\n"
+            "r = M._hip_runtimes()\nassert len(r) == 1, r\n")
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr

@@ -183,8 +183,9 @@ def test_layer_parity_every_element(name):
     _full_check(inp, layer)
 
 
-def test_layer_parity_int32_ids_and_bad_ids():
-    w = W.PARITY_WORKLOADS["p_ragged"].with_(T=333)
+@pytest.mark.parametrize("name", ["p_ragged", "p_wide"])  # K = 3 (any-K combine), K = 4 (per-K)
+def test_layer_parity_int32_ids_and_bad_ids(name):
+    w = W.PARITY_WORKLOADS[name].with_(T=333)
     inp = W.make_inputs(w, ids_dtype=np.int32, router=oracle.route)
     inp.ids[5, 1] = w.E + 3
     inp.ids[77, 0] = -1
@@ -322,6 +323,8 @@ DEGENERATE = [
     (512, 128, 192, 2, 1, "even", 15),
     (257, 64, 128, 1, 1, "even", 16),
     (64, 64, 64, 1024, 64, "uniform_distinct", 17),  # the largest E and K: 1024 tiny segments
+    (200, 128, 64, 9, 6, "uniform_distinct", 18),    # K = 6: combine kernels compiled for K
+    (100, 64, 64, 20, 13, "uniform_distinct", 19),   # K = 13: one 8-slot group and a remainder
 ]
 
 
