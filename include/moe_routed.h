@@ -63,15 +63,15 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* moe_shape.ids_dtype */
 #define MOE_IDS_I32 0
 #define MOE_IDS_I64 1
 
-/* moe_shape.flags: keep the forward intermediates (xg, h13, a, y) in the saved buffer so that
- * moe_backward can run. Without it the forward keeps its intermediates in the workspace and
- * stores no h13. */
+/* moe_shape.flags: keep the forward intermediates (h13, a, y; xg too with MOE_KEEP_XG or when x
+ * spans 4 GiB or more) in the saved buffer so that moe_backward can run. Without it the forward keeps its
+ * intermediates in the workspace and stores no h13. */
 #define MOE_SAVE_FOR_BACKWARD 1
 /* Weight-gradient storage (Dist-MoE, "In-place WGRAD accumulation": gradients accumulate into
  * existing parameter-gradient storage, which is BF16 or FP32, the same dtype for W13 and W2):
@@ -84,11 +84,17 @@ extern "C" {
 /* Recompute instead of saving (TeraMoE introduction and activation-memory table: the fused
  * kernel trades recomputation for activation memory; Dist-MoE "Use graph and checkpoint
  * features": recompute under a fixed launch sequence). With MOE_SAVE_FOR_BACKWARD | MOE_RECOMPUTE
- * the forward keeps only xg and y in the saved buffer (its a goes to the workspace, which the
- * forward then needs), and moe_backward recomputes h13 and a from xg with the same kernel before
+ * the forward keeps only y (and xg when it is kept at all) in the saved buffer (its a goes to the
+ * workspace, which the forward then needs), and moe_backward recomputes h13 and a from x (or xg)
+ * with the same kernel before
  * the backward proper: the same bits as the saved ones, so every output is bitwise the one of the
  * saving path, for one more gate/up GEMM. */
 #define MOE_RECOMPUTE 8
+/* Materialize xg: the forward runs the permute (xg[r] = x[t]) and the gate/up GEMM reads xg;
+ * with MOE_SAVE_FOR_BACKWARD xg is kept in the saved buffer and moe_backward reads it instead of
+ * x (x may then be NULL there). Without this flag xg is materialized only when x spans 4 GiB or
+ * more; otherwise the GEMMs gather x's token rows through the plan. */
+#define MOE_KEEP_XG 16
 
 /* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64,
  * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31. */
@@ -153,11 +159,13 @@ moe_status moe_plan(const moe_shape* shape, const void* topk_ids, void* plan, hi
  *   a[r]    = bf16(silu(g) * u)                              (SwiGLU epilogue)
  *   y[r]    = bf16(w2[e] . a[r])                             (down grouped GEMM)
  *   out[t]  = bf16(sum_k scores[t,k] * y[pos[t*K+k]])        (combine, k ascending, fp32)
- * plan: from moe_plan with the same shape and ids. saved (moe_saved_bytes) is required with
+ *  plan: from moe_plan with the same shape and ids. saved (moe_saved_bytes) is required with
  * MOE_SAVE_FOR_BACKWARD, workspace (moe_workspace_bytes) without it; the other may be NULL.
- * Without MOE_SAVE_FOR_BACKWARD (and when x spans less than 4 GiB) the permute is fused into the
- * gate/up GEMM, which reads each routed row's token row of x directly (MoonEP FAQ: tokens go
- * straight to their expert-grouped positions); xg is then never materialized. */
+ * When x spans less than 4 GiB (T*D*2 < 2^32) the permute is fused into the gate/up GEMM, which
+ * reads each routed row's token row of x directly (MoonEP FAQ: tokens go straight to their
+ * expert-grouped positions), and xg is never materialized: the backward's W13 weight gradient
+ * (and the recompute) read x through the plan the same way. Otherwise xg is written (and saved
+ * with MOE_SAVE_FOR_BACKWARD). */
 moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t* x,
                        const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
                        void* saved, void* workspace, hipStream_t stream, const moe_trace* trace);
@@ -169,15 +177,17 @@ moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t*
  *   dg          = bf16(da * u * s * (1 + g*(1 - s)));  du = bf16(da * g * s);  dh13[r] = [dg|du]
  *   dw2[e]      = bf16(sum over e's rows of dy^T a)      (zero for an expert with no rows)
  *   dxg[r]      = bf16(w13[e]^T . dh13[r])                (w13[e] viewed as [2F,D])
- *   dw13[e]     = bf16(sum over e's rows of dh13^T xg)
+ *   dw13[e]     = bf16(sum over e's rows of dh13^T xg)      (xg[r] = x[t], read from x or saved)
  *   dx[t]       = bf16(sum_k dxg[pos[t*K+k]])             (k ascending, fp32)
  * dx is overwritten; dw13 and dw2 are overwritten or accumulated into, bf16 or fp32, as the shape's
  * MOE_WGRAD_* flags say (the accumulation of a call is not atomic with respect to other work on the
  * same buffers: calls that accumulate into one buffer must be ordered, e.g. on one stream).
- * Requires the shape's MOE_SAVE_FOR_BACKWARD and the saved
- * buffer of the matching forward; workspace holds dy/dxg and dh13. */
+ * Requires the shape's MOE_SAVE_FOR_BACKWARD, the saved
+ * buffer of the matching forward and its x (device, [T,D] bf16, unchanged since the forward; may
+ * be NULL when the forward kept xg: MOE_KEEP_XG, or x spanning 4 GiB or more); workspace holds
+ * dy/dxg and dh13. */
 moe_status moe_backward(const moe_shape* shape, const void* plan, const void* saved,
-                        const uint16_t* dout, const float* scores, const uint16_t* w13,
+                        const uint16_t* x, const uint16_t* dout, const float* scores, const uint16_t* w13,
                         const uint16_t* w2, uint16_t* dx, void* dw13, void* dw2,
                         float* dscores, void* workspace, hipStream_t stream,
                         const moe_trace* trace);
@@ -193,8 +203,9 @@ moe_status moe_plan_status(const moe_shape* shape, const void* plan, int64_t* ba
                            hipStream_t stream);
 
 /* Device pointers to the saved forward intermediates inside saved (for inspection and tests):
- * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. With MOE_RECOMPUTE
- * h13 and a are not saved: *h13 and *a are set to NULL. */
+ * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. Intermediates that
+ * are not saved come back as NULL: h13 and a with MOE_RECOMPUTE, xg unless MOE_KEEP_XG or x
+ * spans 4 GiB or more (the GEMMs then read x through the plan). */
 moe_status moe_saved_views(const moe_shape* shape, void* saved, uint16_t** xg, uint16_t** h13,
                            uint16_t** a, uint16_t** y);
 

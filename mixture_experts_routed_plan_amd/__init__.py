@@ -20,6 +20,7 @@ MOE_SAVE_FOR_BACKWARD = 1
 MOE_WGRAD_ACCUMULATE = 2
 MOE_WGRAD_F32 = 4
 MOE_RECOMPUTE = 8
+MOE_KEEP_XG = 16
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_TRACE_MAX_EVENTS = 8
@@ -103,7 +104,7 @@ def _load():
         "moe_workspace_bytes": (ctypes.c_size_t, [S]),
         "moe_plan": (St, [S, P, P, P, Tr]),
         "moe_forward": (St, [S, P, P, P, P, P, P, P, P, P, Tr]),
-        "moe_backward": (St, [S, P, P, P, P, P, P, P, P, P, P, P, P, Tr]),
+        "moe_backward": (St, [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Tr]),
         "moe_plan_export": (St, [S, P, P, P, P, P, P]),
         "moe_plan_status": (St, [S, P, ctypes.POINTER(ctypes.c_int64), P]),
         "moe_saved_views": (St, [S, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
@@ -148,10 +149,11 @@ def _stream(stream):
 
 
 def make_shape(T, D, F, E, K, ids_dtype=MOE_IDS_I64, save_for_backward=True,
-               wgrad_accumulate=False, wgrad_f32=False, recompute=False) -> moe_shape:
+               wgrad_accumulate=False, wgrad_f32=False, recompute=False,
+               keep_xg=False) -> moe_shape:
     flags = ((MOE_SAVE_FOR_BACKWARD if save_for_backward else 0)
              | (MOE_WGRAD_ACCUMULATE if wgrad_accumulate else 0) | (MOE_WGRAD_F32 if wgrad_f32 else 0)
-             | (MOE_RECOMPUTE if recompute else 0))
+             | (MOE_RECOMPUTE if recompute else 0) | (MOE_KEEP_XG if keep_xg else 0))
     return moe_shape(int(T), int(D), int(F), int(E), int(K), int(ids_dtype), flags)
 
 
@@ -187,9 +189,9 @@ def moe_forward(shape, plan, x, scores, w13, w2, out, saved=None, workspace=None
                             None if trace is None else ctypes.byref(trace))
 
 
-def moe_backward(shape, plan, saved, dout, scores, w13, w2, dx, dw13, dw2, dscores, workspace,
+def moe_backward(shape, plan, saved, x, dout, scores, w13, w2, dx, dw13, dw2, dscores, workspace,
                  stream=None, trace=None) -> int:
-    return _lib.moe_backward(ctypes.byref(shape), _ptr(plan), _ptr(saved), _ptr(dout),
+    return _lib.moe_backward(ctypes.byref(shape), _ptr(plan), _ptr(saved), _ptr(x), _ptr(dout),
                              _ptr(scores), _ptr(w13), _ptr(w2), _ptr(dx), _ptr(dw13), _ptr(dw2),
                              _ptr(dscores), _ptr(workspace), _stream(stream),
                              None if trace is None else ctypes.byref(trace))

@@ -13,7 +13,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
   if (s->ids_dtype != MOE_IDS_I32 && s->ids_dtype != MOE_IDS_I64) return MOE_E_DTYPE;
-  if (s->flags & ~(MOE_SAVE_FOR_BACKWARD | MOE_WGRAD_ACCUMULATE | MOE_WGRAD_F32 | MOE_RECOMPUTE))
+  if (s->flags &
+      ~(MOE_SAVE_FOR_BACKWARD | MOE_WGRAD_ACCUMULATE | MOE_WGRAD_F32 | MOE_RECOMPUTE | MOE_KEEP_XG))
     return MOE_E_DTYPE;
   if (s->T < 1 || s->K < 1 || s->K > MOE_MAX_TOPK) return MOE_E_SHAPE;
   if (s->E < 1 || s->E > MOE_MAX_EXPERTS) return MOE_E_SHAPE;
@@ -113,11 +114,12 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
     return MOE_E_ALIGN;
   const PlanLayout L = plan_layout(*s);
   const PlanPtrs p = plan_ptrs(L, (void*)plan);
-  uint16_t *xg, *h13 = nullptr, *a, *y;
+  const bool gx = gather_x(*s);
+  uint16_t *xg = nullptr, *h13 = nullptr, *a, *y;
   if (save) {
     const SavedLayout S = saved_layout(*s);
     char* b = (char*)saved;
-    xg = (uint16_t*)(b + S.xg);
+    if (!gx) xg = (uint16_t*)(b + S.xg);
     y = (uint16_t*)(b + S.y);
     if (re) {  // h13 is not kept; a lives in the workspace until W2 has read it
       a = (uint16_t*)((char*)workspace + work_layout(*s).a);
@@ -128,13 +130,13 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
   } else {
     const WorkLayout W = work_layout(*s);
     char* b = (char*)workspace;
-    xg = (uint16_t*)(b + W.xg);
+    if (!gx) xg = (uint16_t*)(b + W.xg);
     a = (uint16_t*)(b + W.a);
     y = (uint16_t*)(b + W.y);
   }
   Tracer tr{trace, stream, 0};
   MOE_TRY(tr.mark());
-  if (fused_permute(*s)) {
+  if (gx) {
     // no xg: the gate/up GEMM reads each routed row's token row of x (the permute stage is empty)
     MOE_TRY(tr.mark());
     MOE_TRY(launch_fprop_w13(*s, p, x, w13, h13, a, stream, true));
@@ -152,19 +154,22 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
 }
 
 moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
-                        const uint16_t* dout, const float* scores, const uint16_t* w13,
+                        const uint16_t* x, const uint16_t* dout, const float* scores,
+                        const uint16_t* w13,
                         const uint16_t* w2, uint16_t* dx, void* dw13, void* dw2,
                         float* dscores, void* workspace, hipStream_t stream,
                         const moe_trace* trace) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return MOE_E_STATE;
-  if (!plan || !saved || !dout || !scores || !w13 || !w2 || !dx || !dw13 || !dw2 || !dscores ||
-      !workspace)
+  const bool gx = gather_x(*s);  // the GEMMs that read xg read x's token rows (xg is not saved)
+  if (!plan || !saved || (gx && !x) || !dout || !scores || !w13 || !w2 || !dx || !dw13 || !dw2 ||
+      !dscores || !workspace)
     return MOE_E_NULL;
-  if (!aligned(plan, 16) || !aligned(saved, 16) || !aligned(dout, 16) || !aligned(w13, 16) ||
-      !aligned(w2, 16) || !aligned(dx, 16) || !aligned(dw13, 16) || !aligned(dw2, 16) ||
-      !aligned(workspace, 16) || !aligned(scores, 4) || !aligned(dscores, 4))
+  if (!aligned(plan, 16) || !aligned(saved, 16) || (x && !aligned(x, 16)) || !aligned(dout, 16) ||
+      !aligned(w13, 16) || !aligned(w2, 16) || !aligned(dx, 16) || !aligned(dw13, 16) ||
+      !aligned(dw2, 16) || !aligned(workspace, 16) || !aligned(scores, 4) ||
+      !aligned(dscores, 4))
     return MOE_E_ALIGN;
   const PlanLayout L = plan_layout(*s);
   const PlanPtrs p = plan_ptrs(L, (void*)plan);
@@ -173,7 +178,7 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   const char* sb = (const char*)saved;
   const WorkLayout W = work_layout(*s);
   char* wb = (char*)workspace;
-  const uint16_t* xg = (const uint16_t*)(sb + S.xg);
+  const uint16_t* xg = gx ? x : (const uint16_t*)(sb + S.xg);
   const uint16_t* y = (const uint16_t*)(sb + S.y);
   uint16_t* dy = (uint16_t*)(wb + W.dy);
   uint16_t* dh13 = (uint16_t*)(wb + W.dh13);
@@ -187,7 +192,7 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   MOE_TRY(launch_combine_bwd(*s, p.pos, dout, y, scores, dy, dscores, stream));
   MOE_TRY(tr.mark());
   if (re) {
-    MOE_TRY(launch_fprop_w13(*s, p, xg, w13, dh13, (uint16_t*)(wb + W.a_re), stream));
+    MOE_TRY(launch_fprop_w13(*s, p, xg, w13, dh13, (uint16_t*)(wb + W.a_re), stream, gx));
     MOE_TRY(tr.mark());
   }
   MOE_TRY(launch_dgrad_w2(*s, p, dy, w2, h13, dh13, stream));
@@ -196,7 +201,7 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   MOE_TRY(tr.mark());
   MOE_TRY(launch_dgrad_w13(*s, p, dh13, w13, dxg, stream));
   MOE_TRY(tr.mark());
-  MOE_TRY(launch_wgrad_w13(*s, p, dh13, xg, dw13, stream));
+  MOE_TRY(launch_wgrad_w13(*s, p, dh13, xg, dw13, stream, gx));
   MOE_TRY(tr.mark());
   MOE_TRY(launch_combine(*s, p.pos, dxg, nullptr, dx, stream));
   MOE_TRY(tr.mark());
@@ -269,7 +274,7 @@ moe_status moe_saved_views(const moe_shape* s, void* saved, uint16_t** xg, uint1
   const SavedLayout S = saved_layout(*s);
   char* b = (char*)saved;
   const bool re = (s->flags & MOE_RECOMPUTE) != 0;
-  if (xg) *xg = (uint16_t*)(b + S.xg);
+  if (xg) *xg = gather_x(*s) ? nullptr : (uint16_t*)(b + S.xg);
   if (h13) *h13 = re ? nullptr : (uint16_t*)(b + S.h13);
   if (a) *a = re ? nullptr : (uint16_t*)(b + S.a);
   if (y) *y = (uint16_t*)(b + S.y);

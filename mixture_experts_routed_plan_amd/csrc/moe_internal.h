@@ -53,12 +53,19 @@ inline PlanLayout plan_layout(const moe_shape& s) {
   return L;
 }
 
+// Unless MOE_KEEP_XG asks for xg, and when x spans less than 4 GiB (32-bit copy offsets from the
+// base of x), the GEMMs that would read xg gather x's token rows through the plan's src instead,
+// so xg is never materialized
+inline bool gather_x(const moe_shape& s) {
+  return !(s.flags & MOE_KEEP_XG) && (uint64_t)s.T * (uint64_t)s.D * 2 < (1ull << 32);
+}
+
 struct SavedLayout {
   size_t xg, h13, a, y, total;
 };
 
-// With MOE_RECOMPUTE only xg and y are saved (h13 and a are recomputed in the backward); the
-// h13 and a offsets are then unused.
+// With MOE_RECOMPUTE h13 and a are not saved (recomputed in the backward), and with gather_x no
+// xg; the offsets of what is not saved are unused.
 inline SavedLayout saved_layout(const moe_shape& s) {
   SavedLayout L{};
   const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
@@ -69,7 +76,7 @@ inline SavedLayout saved_layout(const moe_shape& s) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.xg = take(2 * N * D);
+  L.xg = gather_x(s) ? 0 : take(2 * N * D);
   L.h13 = re ? 0 : take(2 * N * 2 * F);
   L.a = re ? 0 : take(2 * N * F);
   L.y = take(2 * N * D);
@@ -77,15 +84,10 @@ inline SavedLayout saved_layout(const moe_shape& s) {
   return L;
 }
 
-// the forward without saving gathers token rows inside the gate/up GEMM when x spans < 4 GiB
-inline bool fused_permute(const moe_shape& s) {
-  return !(s.flags & MOE_SAVE_FOR_BACKWARD) && (uint64_t)s.T * (uint64_t)s.D * 2 < (1ull << 32);
-}
-
-// Workspace: the forward without saving keeps xg, a, y here (with MOE_RECOMPUTE only a); the
-// backward keeps dy (later reused for dxg, once dy is dead) and dh13; with MOE_RECOMPUTE also the
-// recomputed a (a_re), and the recomputed h13 sits where dh13 goes (the SwiGLU-derivative GEMM
-// reads each g, u and writes its dg, du in place).
+// Workspace: the forward without saving keeps xg (unless gather_x), a, y here (with MOE_RECOMPUTE
+// only a); the backward keeps dy (later reused for dxg, once dy is dead) and dh13; with
+// MOE_RECOMPUTE also the recomputed a (a_re), and the recomputed h13 sits where dh13 goes (the
+// SwiGLU-derivative GEMM reads each g, u and writes its dg, du in place).
 struct WorkLayout {
   size_t xg, a, y, fwd_total;
   size_t dy, dh13, a_re, bwd_total;
@@ -96,7 +98,7 @@ inline WorkLayout work_layout(const moe_shape& s) {
   WorkLayout L{};
   const size_t N = (size_t)(s.T * s.K), D = (size_t)s.D, F = (size_t)s.F;
   L.xg = 0;
-  L.a = fused_permute(s) ? 0 : align_up(2 * N * D, 256);  // no xg when the permute is fused
+  L.a = gather_x(s) ? 0 : align_up(2 * N * D, 256);  // no xg when the permute is fused
   L.y = L.a + align_up(2 * N * F, 256);
   L.fwd_total = L.y + align_up(2 * N * D, 256);
   L.dy = 0;
@@ -196,7 +198,8 @@ hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
                            const uint16_t* a, void* dw2, hipStream_t st);
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st);
+// gather: xg is x and the k rows are gathered through the plan's src (no xg)
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
-                            const uint16_t* xg, void* dw13, hipStream_t st);
+                            const uint16_t* xg, void* dw13, hipStream_t st, bool gather = false);
 
 }  // namespace moe

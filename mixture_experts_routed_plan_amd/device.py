@@ -29,15 +29,16 @@ class Layer:
 
     def __init__(self, T, D, F, E, K, ids_dtype=np.int64, save_for_backward=True,
                  device="cuda", alloc_grads=None, wgrad_accumulate=False, wgrad_f32=False,
-                 recompute=False):
+                 recompute=False, keep_xg=False):
         self.shape = make_shape(T, D, F, E, K,
                                 MOE_IDS_I64 if np.dtype(ids_dtype) == np.int64 else MOE_IDS_I32,
-                                save_for_backward, wgrad_accumulate, wgrad_f32, recompute)
+                                save_for_backward, wgrad_accumulate, wgrad_f32, recompute, keep_xg)
         s = self.shape
         self.device = device
         nb = moe_plan_bytes(s)
         if nb == 0:
             raise ValueError("shape rejected by the library: %r" % (s,))
+        self.x = None  # the forward's x, kept for the backward
         self.plan_buf = torch.empty(nb, dtype=torch.uint8, device=device)
         sb = moe_saved_bytes(s)
         self.saved = torch.empty(sb, dtype=torch.uint8, device=device) if sb else None
@@ -61,12 +62,14 @@ class Layer:
     def forward(self, x, scores, w13, w2, stream=None, trace=None):
         check(moe_forward(self.shape, self.plan_buf, x, scores, w13, w2, self.out, self.saved,
                           self.workspace, stream, trace), "moe_forward")
+        self.x = x  # the backward reads x again (the W13 weight gradient gathers its token rows)
         return self.out
 
-    def backward(self, dout, scores, w13, w2, stream=None, trace=None):
-        check(moe_backward(self.shape, self.plan_buf, self.saved, dout, scores, w13, w2, self.dx,
-                           self.dw13, self.dw2, self.dscores, self.workspace, stream, trace),
-              "moe_backward")
+    def backward(self, dout, scores, w13, w2, stream=None, trace=None, x=None):
+        x = self.x if x is None else x
+        check(moe_backward(self.shape, self.plan_buf, self.saved, x, dout, scores, w13, w2,
+                           self.dx, self.dw13, self.dw2, self.dscores, self.workspace, stream,
+                           trace), "moe_backward")
 
     # -- inspection ------------------------------------------------------------------------
     def plan_arrays(self):

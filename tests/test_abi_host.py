@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 2
+    assert M.moe_abi_version() == 3
     for st in range(0, -8, -1):
         assert M.moe_status_str(st) != "unknown status"
     assert M.moe_status_str(-99) == "unknown status"
@@ -58,10 +58,13 @@ def test_sizes_are_closed_forms_of_the_shape():
     s = shape()
     N = 64 * 2
     assert M.moe_plan_bytes(s) >= 4 * (8 + 9 + 2 * N)
-    assert M.moe_saved_bytes(s) >= 2 * N * (256 + 2 * 128 + 128 + 256)
+    # h13, a, y; xg only with MOE_KEEP_XG (otherwise the GEMMs read x through the plan)
+    assert M.moe_saved_bytes(s) >= 2 * N * (2 * 128 + 128 + 256)
+    keep = M.make_shape(64, 256, 128, 8, 2, keep_xg=True)
+    assert M.moe_saved_bytes(keep) == M.moe_saved_bytes(s) + 2 * N * 256
     assert M.moe_workspace_bytes(s) >= 2 * N * (256 + 2 * 128)
     assert M.moe_saved_bytes(shape(save_for_backward=False)) == 0
-    # recompute keeps only xg and y, and the backward needs room for the recomputed a
+    # recompute keeps only y (and xg when kept), and the backward needs room for the recomputed a
     re = M.make_shape(64, 256, 128, 8, 2, recompute=True)
     assert M.moe_saved_bytes(re) == M.moe_saved_bytes(s) - 2 * N * (2 * 128 + 128)
     assert M.moe_workspace_bytes(re) >= 2 * N * (256 + 2 * 128 + 128)  # dy, h13/dh13, a
@@ -84,12 +87,12 @@ def test_bad_dtype_and_flags_rejected():
     s.ids_dtype = 7
     assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_DTYPE
     s = shape()
-    s.flags = 16
+    s.flags = 32
     assert M.moe_plan_bytes(s) == 0
     s2 = shape()
     s2.flags = M.MOE_SAVE_FOR_BACKWARD | M.MOE_WGRAD_ACCUMULATE | M.MOE_WGRAD_F32
     assert M.moe_plan_bytes(s2) > 0
-    s.flags = 16
+    s.flags = 32
     assert M.moe_forward(s, 256, 256, 256, 256, 256, 256, 256, 256, 0) == M.MOE_E_DTYPE
 
 
@@ -110,10 +113,13 @@ def test_null_and_alignment_rejected():
     # with recompute the forward also needs the workspace (for a)
     s3 = M.make_shape(64, 256, 128, 8, 2, recompute=True)
     assert M.moe_forward(s3, a, a, a, a, a, a, a, None, 0) == M.MOE_E_NULL
-    args = [a] * 11
-    assert M.moe_backward(s, *args[:3], None, *args[4:11], stream=0) == M.MOE_E_NULL
+    # backward: plan, saved, x, dout, scores, w13, w2, dx, dw13, dw2, dscores, workspace
+    args = [a] * 12
+    assert M.moe_backward(s, *args[:3], None, *args[4:], stream=0) == M.MOE_E_NULL  # dout
+    assert M.moe_backward(s, *args[:2], None, *args[3:], stream=0) == M.MOE_E_NULL  # x
     assert M.moe_backward(s2, *args, stream=0) == M.MOE_E_STATE
-    assert M.moe_backward(s, a, a, a, a, a, a, a + 4, a, a, a, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_backward(s, a, a, a, a, a, a, a, a + 4, a, a, a, a, 0) == M.MOE_E_ALIGN  # dx
+    assert M.moe_backward(s, a, a, a + 2, a, a, a, a, a, a, a, a, a, 0) == M.MOE_E_ALIGN  # x
     assert M.moe_plan_export(s, None, stream=0) == M.MOE_E_NULL
     assert M.moe_plan_status(s, None, 0)[0] == M.MOE_E_NULL
 

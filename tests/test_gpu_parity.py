@@ -80,11 +80,12 @@ def upload(inp, ids_dtype=np.int64):
     return d
 
 
-def run(inp, ids_dtype=np.int64, backward=True, save=True):
+def run(inp, ids_dtype=np.int64, backward=True, save=True, keep_xg=False):
     _, dv = _lib()
     w = inp.w
     d = upload(inp, ids_dtype)
-    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, ids_dtype=ids_dtype, save_for_backward=save)
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, ids_dtype=ids_dtype, save_for_backward=save,
+                     keep_xg=keep_xg)
     layer.plan(d["ids"])
     layer.forward(d["x"], d["scores"], d["w13"], d["w2"])
     if backward:
@@ -162,7 +163,10 @@ def _full_check(inp, layer):
     pl = plan_check(layer, inp.ids, w.E)
     sv = layer.saved_arrays()
     nv = int(ref["offsets"][-1])
-    np.testing.assert_array_equal(sv["xg"][:nv], inp.x[pl["src"][:nv] // w.K])
+    if layer.shape.flags & 16:  # MOE_KEEP_XG: the permute wrote xg and the forward saved it
+        np.testing.assert_array_equal(sv["xg"][:nv], inp.x[pl["src"][:nv] // w.K])
+    else:  # the GEMMs read x through the plan: no xg anywhere
+        assert "xg" not in sv
     assert_close("h13", dv.bits_to_f64(sv["h13"][:nv]), ref["h13"][:nv])
     assert_close("a", dv.bits_to_f64(sv["a"][:nv]), ref["a"][:nv])
     assert_close("y", dv.bits_to_f64(sv["y"][:nv]), ref["y"][:nv])
@@ -174,12 +178,13 @@ def _full_check(inp, layer):
     return ref
 
 
+@pytest.mark.parametrize("keep_xg", [False, True])  # x gathered inside the GEMMs / permute + xg
 @pytest.mark.parametrize("name", FULL_CASES)
-def test_layer_parity_every_element(name):
+def test_layer_parity_every_element(name, keep_xg):
     w = {**W.WORKLOADS, **W.PARITY_WORKLOADS}[name]
     inp = W.make_inputs(w, router=oracle.route)
-    log("\n[%s] T=%d D=%d F=%d E=%d K=%d" % (name, w.T, w.D, w.F, w.E, w.K))
-    layer, _ = run(inp)
+    log("\n[%s] T=%d D=%d F=%d E=%d K=%d keep_xg=%s" % (name, w.T, w.D, w.F, w.E, w.K, keep_xg))
+    layer, _ = run(inp, keep_xg=keep_xg)
     _full_check(inp, layer)
 
 
@@ -248,8 +253,12 @@ def test_large_plan_and_permute_in_full(name):
     inp, layer = _large(name)
     w = inp.w
     pl = plan_check(layer, inp.ids, w.E)
-    sv = layer.saved_arrays()
+    assert "xg" not in layer.saved_arrays()  # the timed configuration gathers x in the GEMMs
+    # the permute (MOE_KEEP_XG) at the same size, every row
+    kl, _ = run(inp, backward=False, save=True, keep_xg=True)
+    sv = kl.saved_arrays()
     np.testing.assert_array_equal(sv["xg"], inp.x[pl["src"] // w.K])
+    del kl, sv
 
 
 @pytest.mark.parametrize("half", [0, 1])
