@@ -70,8 +70,8 @@ class HipEvents:
 
 PLAN_STAGES = ["plan_hist", "plan_scan", "plan_scatter"]
 FWD_STAGES = ["permute", "fprop_w13_swiglu", "fprop_w2", "combine"]
-BWD_STAGES = ["combine_bwd_dscores", "dgrad_w2_swiglu", "wgrad_w2", "dgrad_w13", "wgrad_w13",
-              "dx_combine"]
+BWD_STAGES = ["combine_bwd_dscores", "dgrad_w2_swiglu", "wgrad_w2", "permute_bwd", "wgrad_w13",
+              "dgrad_w13", "dx_combine"]
 # with --recompute the backward rebuilds h13 and a first (one more gate/up GEMM)
 BWD_STAGES_RECOMPUTE = BWD_STAGES[:1] + ["recompute_w13"] + BWD_STAGES[1:]
 
@@ -81,6 +81,7 @@ def stage_work(w):
     N, T, D, F = w.N, w.T, w.D, w.F
     return {
         "permute": ("hbm", 2 * T * D + 2 * N * D),
+        "permute_bwd": ("hbm", 2 * T * D + 2 * N * D),
         "fprop_w13_swiglu": ("mfma", 4 * N * D * F),
         "recompute_w13": ("mfma", 4 * N * D * F),
         "fprop_w2": ("mfma", 2 * N * D * F),
@@ -124,7 +125,8 @@ SRC_FILES = ["mixture_experts_routed_plan_amd/csrc/gemm.hip",
              "mixture_experts_routed_plan_amd/csrc/moe_internal.h"]
 STAGE_KERNEL = {
     "plan_hist": "moe_plan_hist", "plan_scan": "moe_plan_scan", "plan_scatter": "moe_plan_scatter",
-    "permute": "moe_permute", "fprop_w13_swiglu": "moe_fprop_w13_swiglu",
+    "permute": "moe_permute", "permute_bwd": "moe_permute",
+    "fprop_w13_swiglu": "moe_fprop_w13_swiglu",
     "fprop_w2": "moe_fprop_w2", "combine": "moe_combine<true>",
     "combine_bwd_dscores": "moe_combine_bwd_dscores", "dgrad_w2_swiglu": "moe_dgrad_w2_swiglu",
     "wgrad_w2": "moe_wgrad_w2", "dgrad_w13": "moe_dgrad_w13", "wgrad_w13": "moe_wgrad_w13",
@@ -321,6 +323,9 @@ def main():
     ap.add_argument("--skip-extras", action="store_true",
                     help="time only the fwd+bwd step (no forward-only and router lines; for "
                          "profiling runs, so that each kernel's statistics cover the step alone)")
+    ap.add_argument("--keep-xg", action="store_true",
+                    help="materialize xg in the forward and save it (MOE_KEEP_XG) instead of "
+                         "gathering x's token rows inside the gate/up GEMM")
     ap.add_argument("--recompute", action="store_true",
                     help="save only xg and y; the backward recomputes h13 and a")
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "bf16-accumulate", "f32", "f32-accumulate"],
@@ -385,7 +390,13 @@ def main():
     scores = torch.from_numpy(inp.scores).cuda()
     layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, save_for_backward=True,
                      wgrad_accumulate=args.wgrad.endswith("accumulate"),
-                     wgrad_f32=args.wgrad.startswith("f32"), recompute=args.recompute)
+                     wgrad_f32=args.wgrad.startswith("f32"), recompute=args.recompute,
+                     keep_xg=args.keep_xg)
+    # without MOE_KEEP_XG (and with x below 4 GiB) the forward's permute stage is empty and the
+    # backward permutes xg into its workspace; with it, the other way round
+    gathers = not args.keep_xg and 2 * w.T * w.D < 2 ** 32
+    empty = {"permute": "fused: the gate/up GEMM gathers x's token rows, no kernel"} if gathers \
+        else {"permute_bwd": "xg saved by the forward, no kernel"}
     bwd_stages = BWD_STAGES_RECOMPUTE if args.recompute else BWD_STAGES
     stream = torch.cuda.current_stream().cuda_stream
     hip = HipEvents()
@@ -436,7 +447,9 @@ def main():
     for n in names:
         avg = float(np.mean(per[n]))
         ent = {"ms": round(avg, 4)}
-        if n in work:
+        if n in empty:
+            ent["note"] = empty[n]
+        elif n in work:
             kind, amount = work[n]
             if kind == "mfma":
                 ent["tflops"] = round(amount / avg / 1e9, 1)
@@ -445,7 +458,7 @@ def main():
                 ent["gbs"] = round(amount / avg / 1e6, 1)
                 ent["frac_peak"] = round(amount / avg / 1e6 / PEAK_HBM_GBS, 4)
         stages[n] = ent
-    dom = max((n for n in work if n in stages), key=lambda n: stages[n]["ms"])
+    dom = max((n for n in work if n in stages and n not in empty), key=lambda n: stages[n]["ms"])
     kind, amount = work[dom]
     avg_s = stages[dom]["ms"] / 1e3
     if kind == "mfma":
@@ -482,6 +495,7 @@ def main():
                                % (w.name, w.T, w.D, w.F, w.E, w.K),
                    "T": w.T, "D": w.D, "F": w.F, "E": w.E, "K": w.K,
                    "routing": w.routing, "wgrad": args.wgrad, "recompute": args.recompute,
+                   "keep_xg": args.keep_xg,
                    "parallelism": "single GPU (one EP rank's share)"},
         "roofline": roof,
         "stages": stages,

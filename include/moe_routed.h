@@ -126,10 +126,12 @@ typedef enum moe_status {
  * events[0] on the stream before its first kernel and events[s+1] after stage s, for the first
  * n_events events (the caller creates the events). Stages:
  *   moe_plan:     0 block histograms, 1 scan + tile tables, 2 stable scatter
- *   moe_forward:  0 permute, 1 W13 GEMM + SwiGLU, 2 W2 GEMM, 3 combine
- *   moe_backward: 0 combine transpose + dscores, 1 DGRAD W2 + SwiGLU derivative, 2 WGRAD W2,
- *                 3 DGRAD W13, 4 WGRAD W13, 5 dX combine                                         */
-#define MOE_TRACE_MAX_EVENTS 8
+ *   moe_forward:  0 permute (empty when the gate/up GEMM gathers x), 1 W13 GEMM + SwiGLU,
+ *                 2 W2 GEMM, 3 combine
+ *   moe_backward: 0 combine transpose + dscores, [with MOE_RECOMPUTE: the W13 GEMM + SwiGLU
+ *                 again], then DGRAD W2 + SwiGLU derivative, WGRAD W2, permute of xg (empty when
+ *                 xg was saved), WGRAD W13, DGRAD W13, dX combine                                 */
+#define MOE_TRACE_MAX_EVENTS 16
 typedef struct moe_trace {
   int32_t n_events;
   hipEvent_t events[MOE_TRACE_MAX_EVENTS];
@@ -171,7 +173,9 @@ moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t*
                        void* saved, void* workspace, hipStream_t stream, const moe_trace* trace);
 
 /* Backward of moe_forward (Dist-MoE: DGRAD and WGRAD; MegaMoE "Design": the down projection's
- * weight gradient is produced before the gate/up one), given dout[T,D]:
+ * weight gradient is produced before the gate/up one; here the gate/up weight gradient also runs
+ * before dxg, so that xg, when it was not saved, is permuted from x into the workspace region
+ * that dy no longer needs and dxg takes next), given dout[T,D]:
  *   dy[r]       = bf16(scores[t,k] * dout[t]);   dscores[t,k] = sum_d dout[t,d] * y[r,d]  (fp32)
  *   da[r]       = w2[e]^T . dy[r]   (fp32, not stored);   with s = sigmoid(g):
  *   dg          = bf16(da * u * s * (1 + g*(1 - s)));  du = bf16(da * g * s);  dh13[r] = [dg|du]

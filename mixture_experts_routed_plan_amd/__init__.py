@@ -23,7 +23,7 @@ MOE_RECOMPUTE = 8
 MOE_KEEP_XG = 16
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
-MOE_TRACE_MAX_EVENTS = 8
+MOE_TRACE_MAX_EVENTS = 16
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 MOE_MAX_GROUPS = 64

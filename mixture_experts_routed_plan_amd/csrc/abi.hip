@@ -178,11 +178,14 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   const char* sb = (const char*)saved;
   const WorkLayout W = work_layout(*s);
   char* wb = (char*)workspace;
-  const uint16_t* xg = gx ? x : (const uint16_t*)(sb + S.xg);
   const uint16_t* y = (const uint16_t*)(sb + S.y);
   uint16_t* dy = (uint16_t*)(wb + W.dy);
   uint16_t* dh13 = (uint16_t*)(wb + W.dh13);
-  uint16_t* dxg = dy;  // dy is dead once the W2 weight gradient has been formed
+  // dy is dead once the W2 weight gradient has been formed: its region then holds xg for the W13
+  // weight gradient (gather_x: permuted there from x; otherwise xg is the saved one) and, after
+  // that GEMM, dxg
+  uint16_t* dxg = dy;
+  const uint16_t* xg = gx ? dy : (const uint16_t*)(sb + S.xg);
   // recompute: h13 is rebuilt where dh13 goes (read and overwritten element by element by the
   // SwiGLU-derivative GEMM), a in its own workspace region
   const uint16_t* h13 = re ? dh13 : (const uint16_t*)(sb + S.h13);
@@ -192,16 +195,19 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   MOE_TRY(launch_combine_bwd(*s, p.pos, dout, y, scores, dy, dscores, stream));
   MOE_TRY(tr.mark());
   if (re) {
-    MOE_TRY(launch_fprop_w13(*s, p, xg, w13, dh13, (uint16_t*)(wb + W.a_re), stream, gx));
+    MOE_TRY(launch_fprop_w13(*s, p, gx ? x : xg, w13, dh13, (uint16_t*)(wb + W.a_re), stream,
+                             gx));
     MOE_TRY(tr.mark());
   }
   MOE_TRY(launch_dgrad_w2(*s, p, dy, w2, h13, dh13, stream));
   MOE_TRY(tr.mark());
   MOE_TRY(launch_wgrad_w2(*s, p, dy, a, dw2, stream));
   MOE_TRY(tr.mark());
-  MOE_TRY(launch_dgrad_w13(*s, p, dh13, w13, dxg, stream));
+  if (gx) MOE_TRY(launch_permute(*s, p.pos, x, dy, stream));  // the stage is empty otherwise
   MOE_TRY(tr.mark());
-  MOE_TRY(launch_wgrad_w13(*s, p, dh13, xg, dw13, stream, gx));
+  MOE_TRY(launch_wgrad_w13(*s, p, dh13, xg, dw13, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_dgrad_w13(*s, p, dh13, w13, dxg, stream));
   MOE_TRY(tr.mark());
   MOE_TRY(launch_combine(*s, p.pos, dxg, nullptr, dx, stream));
   MOE_TRY(tr.mark());

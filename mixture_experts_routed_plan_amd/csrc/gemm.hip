@@ -254,17 +254,6 @@ struct MnTile {
     if (k > klim - 1) k = klim - 1;  // k0 <= klim - 1 whenever the stage exists
     dma16(base + (int64_t)k0 * ldb, (uint32_t)((k - k0) * ldb) + col[i], lds_tile + blk * 2 * R * 2);
   }
-  // gathered rows: the tile's k rows are rows of the base matrix picked by the caller; krow gives
-  // copy i's k row (clamped as above) and issue_row copies it from row `src_row` of the base
-  // (byte offset src_row * ldb, which the host keeps below 4 GiB)
-  __device__ __forceinline__ int krow(int k0, int klim, int i) const {
-    const int k = k0 + row[i];
-    return k > klim - 1 ? klim - 1 : k;
-  }
-  __device__ __forceinline__ void issue_row(uint32_t lds_tile, int src_row, int i) const {
-    const int blk = (threadIdx.x >> 6) * NB + i;
-    dma16(base, (uint32_t)src_row * (uint32_t)ldb + col[i], lds_tile + blk * 2 * R * 2);
-  }
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -287,10 +276,7 @@ __device__ __forceinline__ v4i16 read_mn_half(const uint16_t* tile, int idx0, in
 
 // ---- the kernel -------------------------------------------------------------------------------
 
-// QG: the Q operand is idx-contiguous and its k rows are gathered: routed row r of the expert's
-// segment reads row gather_src[r] / gather_k of Q (WGRAD W13 reading x instead of xg)
-template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI, int OUT = OUT_BF16,
-          bool QG = false>
+template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI, int OUT = OUT_BF16>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   constexpr int WR = kWaves / 2;  // wavefront rows (P) x 2 wavefront columns (Q)
   constexpr int WM = BM / WR, WN = BN / 2, FM = WM / 32, FN = WN / 32;
@@ -364,10 +350,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       return (uint32_t)((int64_t)wrow * ldb);
     });
   } else {
-    if constexpr (QG)
-      qm.init(g.Q + t.n0, g.ldq, 0, g.N_out - t.n0);
-    else
-      qm.init(qbase + (int64_t)t.kbeg * g.ldq + t.n0, g.ldq, 0, g.N_out - t.n0);
+    qm.init(qbase + (int64_t)t.kbeg * g.ldq + t.n0, g.ldq, 0, g.N_out - t.n0);
   }
 
   f32x16 acc[FN][FM];
@@ -388,25 +371,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // copy of one stage: NBO DMA blocks per operand and wavefront
   constexpr int NBO = DmaTile<BM>::NB, NC = 2 * NBO;
   static_assert(DmaTile<BM>::NB == MnTile<BM>::NB && DmaTile<BN>::NB == NBO, "copies per operand");
-  // QG: qsrc[i] holds gather_src of the routed row that Q copy i of the next stage to be issued
-  // reads; it is loaded one stage ahead of its use (right after the previous use)
-  int qsrc[QG ? NBO : 1];
-  auto load_qsrc = [&](int kt, int i) {
-    if constexpr (QG) qsrc[i] = g.gather_src[t.kbeg + qm.krow(kt * BK, klen, i)];
-  };
   auto copy_issue = [&](int b, int kt, int n) {
     const int k0 = kt * BK;  // relative to kbeg
     if (n < NBO) {
       if constexpr (P_KC) pd.issue(addrP(b), t.kbeg + k0, n); else pm.issue(addrP(b), k0, klen, n);
     } else {
-      if constexpr (Q_KC) {
-        qd.issue(addrQ(b), t.kbeg + k0, n - NBO);
-      } else if constexpr (QG) {
-        qm.issue_row(addrQ(b), qsrc[n - NBO] / g.gather_k, n - NBO);
-        load_qsrc(kt + 1, n - NBO);
-      } else {
-        qm.issue(addrQ(b), k0, klen, n - NBO);
-      }
+      if constexpr (Q_KC) qd.issue(addrQ(b), t.kbeg + k0, n - NBO); else qm.issue(addrQ(b), k0, klen, n - NBO);
     }
   };
 
@@ -521,10 +491,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
   };
   if (nk > 0) {
-    if constexpr (QG) {
-#pragma unroll
-      for (int i = 0; i < NBO; ++i) load_qsrc(0, i);
-    }
 #pragma unroll
     for (int n = 0; n < NC; ++n) copy_issue(0, 0, n);
     __builtin_amdgcn_s_waitcnt(0);
@@ -771,31 +737,22 @@ MOE_GEMM_KERNEL(moe_wgrad_w2, false, false, SCHED_KSEG, EPI_STORE)
 MOE_GEMM_KERNEL(moe_wgrad_w13, false, false, SCHED_KSEG, EPI_STORE)
 
 // weight gradients accumulated into existing storage, or kept in fp32
-#define MOE_WGRAD_KERNEL(name, OUT, QG)                                                         \
+#define MOE_WGRAD_KERNEL(name, OUT)                                                             \
   __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void name( \
       GemmArgs g) {                                                                            \
-    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT, QG>(g);                      \
+    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(g);                          \
   }
 
-MOE_WGRAD_KERNEL(moe_wgrad_w2_accum, OUT_BF16_ACC, false)
-MOE_WGRAD_KERNEL(moe_wgrad_w2_f32, OUT_F32, false)
-MOE_WGRAD_KERNEL(moe_wgrad_w2_f32_accum, OUT_F32_ACC, false)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_accum, OUT_BF16_ACC, false)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_f32, OUT_F32, false)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_f32_accum, OUT_F32_ACC, false)
-// WGRAD W13 reading the token rows of x through the plan's src (no xg)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_gx, OUT_BF16, true)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_gx_accum, OUT_BF16_ACC, true)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_gx_f32, OUT_F32, true)
-MOE_WGRAD_KERNEL(moe_wgrad_w13_gx_f32_accum, OUT_F32_ACC, true)
+MOE_WGRAD_KERNEL(moe_wgrad_w2_accum, OUT_BF16_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w2_f32, OUT_F32)
+MOE_WGRAD_KERNEL(moe_wgrad_w2_f32_accum, OUT_F32_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_accum, OUT_BF16_ACC)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_f32, OUT_F32)
+MOE_WGRAD_KERNEL(moe_wgrad_w13_f32_accum, OUT_F32_ACC)
 
 // kernel of a weight-gradient GEMM for the shape's storage flags
-void (*wgrad_kernel(const moe_shape& s, bool w13, bool gather = false))(GemmArgs) {
+void (*wgrad_kernel(const moe_shape& s, bool w13))(GemmArgs) {
   const bool acc = (s.flags & MOE_WGRAD_ACCUMULATE) != 0, f32 = (s.flags & MOE_WGRAD_F32) != 0;
-  if (w13 && gather) {
-    if (f32) return acc ? moe_wgrad_w13_gx_f32_accum : moe_wgrad_w13_gx_f32;
-    return acc ? moe_wgrad_w13_gx_accum : moe_wgrad_w13_gx;
-  }
   if (w13) {
     if (f32) return acc ? moe_wgrad_w13_f32_accum : moe_wgrad_w13_f32;
     return acc ? moe_wgrad_w13_accum : moe_wgrad_w13;
@@ -893,19 +850,15 @@ hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
 }
 
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
-                            const uint16_t* xg, void* dw13, hipStream_t st, bool gather) {
+                            const uint16_t* xg, void* dw13, hipStream_t st) {
   GemmArgs g{};
   g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
   g.P = dh13; g.ldp = 2 * s.F;  // [k = routed row][r = j]
-  g.Q = xg; g.ldq = s.D;        // [k = routed row][c = d]; with gather: x, row src[r] / K
-  if (gather) {
-    g.gather_src = p.src;
-    g.gather_k = (int)s.K;
-  }
+  g.Q = xg; g.ldq = s.D;        // [k = routed row][c = d]
   g.C = (uint16_t*)dw13; g.Cf = (float*)dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
   g.M_out = (int)(2 * s.F); g.N_out = (int)s.D;
   const int grid = (int)(s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN));
-  return launch(wgrad_kernel(s, true, gather), g, grid, st);
+  return launch(wgrad_kernel(s, true), g, grid, st);
 }
 
 }  // namespace moe

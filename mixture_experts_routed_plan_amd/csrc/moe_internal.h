@@ -54,8 +54,9 @@ inline PlanLayout plan_layout(const moe_shape& s) {
 }
 
 // Unless MOE_KEEP_XG asks for xg, and when x spans less than 4 GiB (32-bit copy offsets from the
-// base of x), the GEMMs that would read xg gather x's token rows through the plan's src instead,
-// so xg is never materialized
+// base of x), the gate/up GEMM gathers x's token rows through the plan's src instead of reading
+// xg, so the forward neither permutes nor saves xg (the backward permutes it into its workspace
+// for the W13 weight gradient)
 inline bool gather_x(const moe_shape& s) {
   return !(s.flags & MOE_KEEP_XG) && (uint64_t)s.T * (uint64_t)s.D * 2 < (1ull << 32);
 }
@@ -85,9 +86,10 @@ inline SavedLayout saved_layout(const moe_shape& s) {
 }
 
 // Workspace: the forward without saving keeps xg (unless gather_x), a, y here (with MOE_RECOMPUTE
-// only a); the backward keeps dy (later reused for dxg, once dy is dead) and dh13; with
-// MOE_RECOMPUTE also the recomputed a (a_re), and the recomputed h13 sits where dh13 goes (the
-// SwiGLU-derivative GEMM reads each g, u and writes its dg, du in place).
+// only a); the backward keeps dy and dh13, and once dy is dead (after the W2 weight gradient) its
+// region holds xg for the W13 weight gradient (gather_x: permuted there from x) and then dxg;
+// with MOE_RECOMPUTE also the recomputed a (a_re), and the recomputed h13 sits where dh13 goes
+// (the SwiGLU-derivative GEMM reads each g, u and writes its dg, du in place).
 struct WorkLayout {
   size_t xg, a, y, fwd_total;
   size_t dy, dh13, a_re, bwd_total;
@@ -198,8 +200,7 @@ hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
                            const uint16_t* a, void* dw2, hipStream_t st);
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st);
-// gather: xg is x and the k rows are gathered through the plan's src (no xg)
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
-                            const uint16_t* xg, void* dw13, hipStream_t st, bool gather = false);
+                            const uint16_t* xg, void* dw13, hipStream_t st);
 
 }  // namespace moe
