@@ -9,23 +9,25 @@
 //
 //   GEMM          rows r          cols c         k            P layout      Q layout      epilogue
 //   W13 FPROP     routed rows     f (gate & up)  d            xg  [r][k]    w13[e] [c][k]  SwiGLU
+//                 (xg[r] = x[src[r] / K]: with a gather list the row copies read x directly)
 //   W2  FPROP     routed rows     d              f            a   [r][k]    w2[e]  [c][k]  store y
 //   W2  DGRAD     routed rows     f              d            dy  [r][k]    w2[e]  [k][c]  SwiGLU'
 //   W13 DGRAD     routed rows     d              j (2F)       dh13[r][k]    w13[e] [k][c]  store dxg
 //   W2  WGRAD     d               f              e's rows     dy  [k][r]    a      [k][c]  store dW2
 //   W13 WGRAD     j (2F)          d              e's rows     dh13[k][r]    xg     [k][c]  store dW13
 //
-// Tiles: BM x BN outputs per 256-thread workgroup, 2x2 wavefronts each owning BM/2 x BN/2, built
-// from v_mfma_f32_32x32x16_bf16. The MFMA's A operand is the Q tile and its B operand the P tile, so
-// each lane ends up holding 4 consecutive output columns of one output row (8-byte stores).
-// K advances 64 at a time through a double-buffered LDS tile [rows][64] whose 16-byte chunks are
-// XOR-swizzled (chunk ^ ((row ^ row>>3) & 7)) so that fragment reads (32 consecutive rows, one
-// chunk) and tile writes are free of bank conflicts.
+// Tiles: 256 x 256 outputs per 512-thread workgroup, 8 wavefronts (two per SIMD) in 4 row groups x
+// 2 column halves, each owning 64 x 128 outputs, built from v_mfma_f32_32x32x16_bf16. The MFMA's A
+// operand is the Q tile and its B operand the P tile, so each lane ends up holding 4 consecutive
+// output columns of one output row. K advances 64 at a time through two LDS stages of 64 KiB,
+// filled by LDS-DMA copies (global_load_lds_dwordx4) one stage ahead of their use.
 //
-// Operands stored k-contiguous ([idx][k]) are copied 16 bytes per lane. Operands stored
-// idx-contiguous ([k][idx]: the transposed weights in DGRAD, both operands of WGRAD) are read as
-// 8x8 blocks (8 rows of 16 bytes), transposed in registers and stored k-contiguous, so one LDS
-// layout and one MFMA loop serve every GEMM.
+// Operands stored k-contiguous ([idx][k]) sit in LDS as [rows][64] with XOR-swizzled 16-byte
+// chunks (chunk ^ ((row ^ row>>3) & 7)), read as 16-byte fragments. Operands stored
+// idx-contiguous ([k][idx]: the transposed weights in DGRAD, both operands of WGRAD) keep that
+// orientation in LDS ([64 k][256 idx], 8-byte chunks swizzled by k) and become MFMA fragments
+// through the LDS transpose read (ds_read_b64_tr_b16), so one MFMA loop serves every GEMM. Both
+// layouts keep fragment reads and copies free of bank conflicts.
 //
 // Scheduling (nothing depends on host-side knowledge of the routing):
 //   * row-ragged GEMMs (FPROP, DGRAD) read the plan's device list of (expert, first row) row
@@ -187,7 +189,7 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
 // k-contiguous operand, copied global -> LDS by DMA: one instruction moves 64 lanes x 16 bytes
 // into 1 KiB of LDS, i.e. 8 rows x 64 k of the tile with lane l landing in row l/8, physical
 // chunk l%8. Each lane therefore fetches the logical chunk that the swizzle stores there. The R/8
-// blocks of a tile are split evenly over the 4 wavefronts (R/32 each). Addresses: a wave-uniform
+// blocks of a tile are split evenly over the wavefronts (R/64 each). Addresses: a wave-uniform
 // base plus a 32-bit byte offset per lane and block.
 template <int R>
 struct DmaTile {
