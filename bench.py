@@ -70,8 +70,8 @@ class HipEvents:
 
 PLAN_STAGES = ["plan_hist", "plan_scan", "plan_scatter"]
 FWD_STAGES = ["permute", "fprop_w13_swiglu", "fprop_w2", "combine"]
-BWD_STAGES = ["combine_bwd_dscores", "dgrad_w2_swiglu", "wgrad_w2", "permute_bwd", "wgrad_w13",
-              "dgrad_w13", "dx_combine"]
+BWD_STAGES = ["combine_bwd_dscores", "w2_backward", "permute_bwd", "wgrad_w13", "dgrad_w13",
+              "dx_combine"]
 # with --recompute the backward rebuilds h13 and a first (one more gate/up GEMM)
 BWD_STAGES_RECOMPUTE = BWD_STAGES[:1] + ["recompute_w13"] + BWD_STAGES[1:]
 
@@ -87,8 +87,7 @@ def stage_work(w):
         "fprop_w2": ("mfma", 2 * N * D * F),
         "combine": ("hbm", 2 * N * D + 2 * T * D),
         "combine_bwd_dscores": ("hbm", 2 * T * D + 4 * N * D),
-        "dgrad_w2_swiglu": ("mfma", 2 * N * D * F),
-        "wgrad_w2": ("mfma", 2 * N * D * F),
+        "w2_backward": ("mfma", 4 * N * D * F),  # DGRAD W2 + SwiGLU' and WGRAD W2, one launch
         "dgrad_w13": ("mfma", 4 * N * D * F),
         "wgrad_w13": ("mfma", 4 * N * D * F),
         "dx_combine": ("hbm", 2 * N * D + 2 * T * D),
@@ -128,8 +127,8 @@ STAGE_KERNEL = {
     "permute": "moe_permute", "permute_bwd": "moe_permute",
     "fprop_w13_swiglu": "moe_fprop_w13_swiglu",
     "fprop_w2": "moe_fprop_w2", "combine": "moe_combine<true>",
-    "combine_bwd_dscores": "moe_combine_bwd_dscores", "dgrad_w2_swiglu": "moe_dgrad_w2_swiglu",
-    "wgrad_w2": "moe_wgrad_w2", "dgrad_w13": "moe_dgrad_w13", "wgrad_w13": "moe_wgrad_w13",
+    "combine_bwd_dscores": "moe_combine_bwd_dscores", "w2_backward": "moe_w2_backward",
+    "dgrad_w13": "moe_dgrad_w13", "wgrad_w13": "moe_wgrad_w13",
     "dx_combine": "moe_combine<false>", "recompute_w13": "moe_fprop_w13_swiglu",
 }
 

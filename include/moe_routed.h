@@ -129,8 +129,8 @@ typedef enum moe_status {
  *   moe_forward:  0 permute (empty when the gate/up GEMM gathers x), 1 W13 GEMM + SwiGLU,
  *                 2 W2 GEMM, 3 combine
  *   moe_backward: 0 combine transpose + dscores, [with MOE_RECOMPUTE: the W13 GEMM + SwiGLU
- *                 again], then DGRAD W2 + SwiGLU derivative, WGRAD W2, permute of xg (empty when
- *                 xg was saved), WGRAD W13, DGRAD W13, dX combine                                 */
+ *                 again], then DGRAD W2 + SwiGLU derivative and WGRAD W2 (one launch), permute
+ *                 of xg (empty when xg was saved), WGRAD W13, DGRAD W13, dX combine              */
 #define MOE_TRACE_MAX_EVENTS 16
 typedef struct moe_trace {
   int32_t n_events;

@@ -199,9 +199,7 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
                              gx));
     MOE_TRY(tr.mark());
   }
-  MOE_TRY(launch_dgrad_w2(*s, p, dy, w2, h13, dh13, stream));
-  MOE_TRY(tr.mark());
-  MOE_TRY(launch_wgrad_w2(*s, p, dy, a, dw2, stream));
+  MOE_TRY(launch_w2_backward(*s, p, dy, w2, h13, dh13, a, dw2, stream));
   MOE_TRY(tr.mark());
   if (gx) MOE_TRY(launch_permute(*s, p.pos, x, dy, stream));  // the stage is empty otherwise
   MOE_TRY(tr.mark());

@@ -51,6 +51,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;  // k per LDS stage
+constexpr int kBM = 256, kBN = 256;  // output tile
+constexpr int kLdsElems = 2 * (kBM + kBN) * kBK;  // two stages (bf16 elements): 128 KiB
 // Wavefronts per workgroup: 8, two per SIMD, each owning 64 x 128 of the 256 x 256 tile (128
 // accumulator registers), so that while one wavefront of a SIMD waits (for LDS data, a copy, the
 // barrier) the other can issue MFMAs.
@@ -112,7 +114,7 @@ struct Tile {
 };
 
 template <int BM, int BN, int SCHED, int EPI>
-__device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
+__device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t, int b) {
   int total, ntn, mtm = 0;
   if (SCHED == SCHED_ROWS) {
     ntn = EPI == EPI_SWIGLU_FWD ? (g.N_out + BN / 2 - 1) / (BN / 2) : (g.N_out + BN - 1) / BN;
@@ -122,7 +124,6 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
     ntn = (g.N_out + BN - 1) / BN;
     total = g.E * mtm * ntn;
   }
-  const int b = blockIdx.x;
   const int full = (total / 256) * 256;
   const int L = b < full ? (b & ~255) + (b & 7) * 32 + ((b & 255) >> 3) : b;
   if (L >= total) return false;
@@ -279,17 +280,18 @@ __device__ __forceinline__ v4i16 read_mn_half(const uint16_t* tile, int idx0, in
 // ---- the kernel -------------------------------------------------------------------------------
 
 template <int BM, int BN, bool P_KC, bool Q_KC, int SCHED, int EPI, int OUT = OUT_BF16>
-__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
+// lds: the kernel's 128 KiB LDS array; b: the tile's index in the launch order of this GEMM
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int b) {
   constexpr int WR = kWaves / 2;  // wavefront rows (P) x 2 wavefront columns (Q)
   constexpr int WM = BM / WR, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int MPK = FN * FM;  // MFMAs per k sub-step and wavefront
   static_assert(BM == 256 && BN == 256, "the interleaved schedule below assumes 256x256 tiles");
   constexpr int BK = kBK;
   constexpr bool MASK_K = SCHED == SCHED_KSEG;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (BM + BN) * BK];
+  static_assert(2 * (BM + BN) * BK == kLdsElems, "LDS stages");
 
   Tile t;
-  if (!decode_tile<BM, BN, SCHED, EPI>(g, t)) return;
+  if (!decode_tile<BM, BN, SCHED, EPI>(g, t, b)) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches
@@ -723,44 +725,56 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   }
 }
 
-constexpr int kBM = 256, kBN = 256;
-
 #define MOE_GEMM_KERNEL(name, P_KC, Q_KC, SCHED, EPI)                                          \
   __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void name( \
       GemmArgs g) {                                                                            \
-    gemm_body<kBM, kBN, P_KC, Q_KC, SCHED, EPI>(g);                                            \
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];                         \
+    gemm_body<kBM, kBN, P_KC, Q_KC, SCHED, EPI>(g, lds, blockIdx.x);                           \
   }
 
 MOE_GEMM_KERNEL(moe_fprop_w13_swiglu, true, true, SCHED_ROWS, EPI_SWIGLU_FWD)
 MOE_GEMM_KERNEL(moe_fprop_w2, true, true, SCHED_ROWS, EPI_STORE)
-MOE_GEMM_KERNEL(moe_dgrad_w2_swiglu, true, false, SCHED_ROWS, EPI_SWIGLU_BWD)
 MOE_GEMM_KERNEL(moe_dgrad_w13, true, false, SCHED_ROWS, EPI_STORE)
-MOE_GEMM_KERNEL(moe_wgrad_w2, false, false, SCHED_KSEG, EPI_STORE)
 MOE_GEMM_KERNEL(moe_wgrad_w13, false, false, SCHED_KSEG, EPI_STORE)
 
 // weight gradients accumulated into existing storage, or kept in fp32
 #define MOE_WGRAD_KERNEL(name, OUT)                                                             \
   __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void name( \
       GemmArgs g) {                                                                            \
-    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(g);                          \
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];                         \
+    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(g, lds, blockIdx.x);         \
   }
 
-MOE_WGRAD_KERNEL(moe_wgrad_w2_accum, OUT_BF16_ACC)
-MOE_WGRAD_KERNEL(moe_wgrad_w2_f32, OUT_F32)
-MOE_WGRAD_KERNEL(moe_wgrad_w2_f32_accum, OUT_F32_ACC)
 MOE_WGRAD_KERNEL(moe_wgrad_w13_accum, OUT_BF16_ACC)
 MOE_WGRAD_KERNEL(moe_wgrad_w13_f32, OUT_F32)
 MOE_WGRAD_KERNEL(moe_wgrad_w13_f32_accum, OUT_F32_ACC)
 
-// kernel of a weight-gradient GEMM for the shape's storage flags
-void (*wgrad_kernel(const moe_shape& s, bool w13))(GemmArgs) {
+// kernel of the W13 weight-gradient GEMM for the shape's storage flags
+void (*wgrad_w13_kernel(const moe_shape& s))(GemmArgs) {
   const bool acc = (s.flags & MOE_WGRAD_ACCUMULATE) != 0, f32 = (s.flags & MOE_WGRAD_F32) != 0;
-  if (w13) {
-    if (f32) return acc ? moe_wgrad_w13_f32_accum : moe_wgrad_w13_f32;
-    return acc ? moe_wgrad_w13_accum : moe_wgrad_w13;
-  }
-  if (f32) return acc ? moe_wgrad_w2_f32_accum : moe_wgrad_w2_f32;
-  return acc ? moe_wgrad_w2_accum : moe_wgrad_w2;
+  if (f32) return acc ? moe_wgrad_w13_f32_accum : moe_wgrad_w13_f32;
+  return acc ? moe_wgrad_w13_accum : moe_wgrad_w13;
+}
+
+// W2 DGRAD (+ SwiGLU derivative) and W2 WGRAD in one launch: the first grid_d workgroups take
+// DGRAD's row tiles (the longer tiles: k = D), the others WGRAD's tiles. Both read dy and write
+// disjoint outputs (dh13, dW2), so WGRAD's tiles run on the CUs that DGRAD's last, partly filled
+// round of workgroups leaves idle. grid_d is a multiple of 8, so that every tile keeps its XCD.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void moe_w2_backward(GemmArgs gd, GemmArgs gw, int grid_d) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
+  const int b = blockIdx.x;
+  if (b < grid_d)
+    gemm_body<kBM, kBN, true, false, SCHED_ROWS, EPI_SWIGLU_BWD>(gd, lds, b);
+  else
+    gemm_body<kBM, kBN, false, false, SCHED_KSEG, EPI_STORE, OUT>(gw, lds, b - grid_d);
+}
+
+void (*w2_backward_kernel(const moe_shape& s))(GemmArgs, GemmArgs, int) {
+  const bool acc = (s.flags & MOE_WGRAD_ACCUMULATE) != 0, f32 = (s.flags & MOE_WGRAD_F32) != 0;
+  if (f32) return acc ? moe_w2_backward<OUT_F32_ACC> : moe_w2_backward<OUT_F32>;
+  return acc ? moe_w2_backward<OUT_BF16_ACC> : moe_w2_backward<OUT_BF16>;
 }
 
 hipError_t launch(void (*kernel)(GemmArgs), const GemmArgs& g, int grid, hipStream_t st) {
@@ -815,17 +829,37 @@ hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
   return launch(moe_fprop_w2, g, rows_grid(s, kBM, ntn), st);
 }
 
-hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
-                           hipStream_t st) {
+static GemmArgs dgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                              const uint16_t* w2, const uint16_t* h13, uint16_t* dh13) {
   GemmArgs g = rows_args(s, p, kBM);
   g.P = dy; g.ldp = s.D;
   g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F;  // w2[e] read as [k = d][c = f]
   g.C = dh13; g.ldc = 2 * s.F;
   g.H = h13; g.ldh = 2 * s.F;
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
-  const int ntn = (int)ceil_div(s.F, kBN);
-  return launch(moe_dgrad_w2_swiglu, g, rows_grid(s, kBM, ntn), st);
+  return g;
+}
+
+static GemmArgs wgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                              const uint16_t* a, void* dw2) {
+  GemmArgs g{};
+  g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
+  g.P = dy; g.ldp = s.D;  // [k = routed row][r = d]
+  g.Q = a; g.ldq = s.F;   // [k = routed row][c = f]
+  g.C = (uint16_t*)dw2; g.Cf = (float*)dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
+  g.M_out = (int)s.D; g.N_out = (int)s.F;
+  return g;
+}
+
+hipError_t launch_w2_backward(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                              const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
+                              const uint16_t* a, void* dw2, hipStream_t st) {
+  const int grid_d = (int)align_up((size_t)rows_grid(s, kBM, (int)ceil_div(s.F, kBN)), 8);
+  const int grid_w = (int)(s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN));
+  hipLaunchKernelGGL(w2_backward_kernel(s), dim3(grid_d + grid_w), dim3(kThreads), 0, st,
+                     dgrad_w2_args(s, p, dy, w2, h13, dh13), wgrad_w2_args(s, p, dy, a, dw2),
+                     grid_d);
+  return hipGetLastError();
 }
 
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
@@ -839,17 +873,6 @@ hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   return launch(moe_dgrad_w13, g, rows_grid(s, kBM, ntn), st);
 }
 
-hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* a, void* dw2, hipStream_t st) {
-  GemmArgs g{};
-  g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
-  g.P = dy; g.ldp = s.D;  // [k = routed row][r = d]
-  g.Q = a; g.ldq = s.F;   // [k = routed row][c = f]
-  g.C = (uint16_t*)dw2; g.Cf = (float*)dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
-  g.M_out = (int)s.D; g.N_out = (int)s.F;
-  const int grid = (int)(s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN));
-  return launch(wgrad_kernel(s, false), g, grid, st);
-}
 
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* xg, void* dw13, hipStream_t st) {
@@ -860,7 +883,7 @@ hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   g.C = (uint16_t*)dw13; g.Cf = (float*)dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
   g.M_out = (int)(2 * s.F); g.N_out = (int)s.D;
   const int grid = (int)(s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN));
-  return launch(wgrad_kernel(s, true), g, grid, st);
+  return launch(wgrad_w13_kernel(s), g, grid, st);
 }
 
 }  // namespace moe

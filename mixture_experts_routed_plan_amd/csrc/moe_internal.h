@@ -192,12 +192,11 @@ hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
 
 hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
                            const uint16_t* w2, uint16_t* y, hipStream_t st);
-hipError_t launch_dgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
-                           hipStream_t st);
-// weight gradients: bf16 or fp32 storage, overwritten or accumulated (shape flags)
-hipError_t launch_wgrad_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
-                           const uint16_t* a, void* dw2, hipStream_t st);
+// W2 DGRAD (+ SwiGLU derivative) and W2 WGRAD in one launch; weight gradients in bf16 or fp32
+// storage, overwritten or accumulated (shape flags)
+hipError_t launch_w2_backward(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
+                              const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
+                              const uint16_t* a, void* dw2, hipStream_t st);
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st);
 hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
