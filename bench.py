@@ -121,6 +121,8 @@ def cpu_baseline(inp, n_tokens):
 SRC_FILES = ["mixture_experts_routed_plan_amd/csrc/gemm.hip",
              "mixture_experts_routed_plan_amd/csrc/rowops.hip",
              "mixture_experts_routed_plan_amd/csrc/plan.hip",
+             "mixture_experts_routed_plan_amd/csrc/router.hip",
+             "mixture_experts_routed_plan_amd/csrc/abi.hip",
              "mixture_experts_routed_plan_amd/csrc/moe_internal.h"]
 STAGE_KERNEL = {
     "plan_hist": "moe_plan_hist", "plan_scan": "moe_plan_scan", "plan_scatter": "moe_plan_scatter",
