@@ -176,6 +176,23 @@ def summarize(prof_dir, out_path, workload, cmd):
     for r in csv.DictReader(open(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))):
         stats[_short_kernel(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                                           float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+    # averages over the timed steps only (the warm-up dispatches, the first warmup/(warmup+steps)
+    # of each kernel's calls in start order, are left out), from the same kernel trace
+    import re
+    import collections
+    joined = " ".join(cmd)
+    m_s, m_w = re.search(r"--steps (\d+)", joined), re.search(r"--warmup (\d+)", joined)
+    n_steps, n_warm = int(m_s.group(1)) if m_s else 5, int(m_w.group(1)) if m_w else 1
+    disp = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(prof_dir, "trace", "run_kernel_trace.csv"))):
+        disp[_short_kernel(r["Kernel_Name"])].append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    timed = {}
+    for k, v in disp.items():
+        v.sort()
+        skip = len(v) * n_warm // (n_warm + n_steps) if len(v) % (n_warm + n_steps) == 0 else 0
+        rest = [d for _, d in v[skip:]]
+        timed[k] = sum(rest) / len(rest) / 1e3
     fetch = _counter_means(os.path.join(prof_dir, "fetch", "run_counter_collection.csv"))
     write = _counter_means(os.path.join(prof_dir, "write", "run_counter_collection.csv"))
     sq = _counter_means(os.path.join(prof_dir, "sq", "run_counter_collection.csv"))
@@ -204,10 +221,11 @@ def summarize(prof_dir, out_path, workload, cmd):
         hit = (c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
                if c.get("TCC_HIT_sum") is not None and (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]) > 0
                else None)
-        table[k] = {"avg_us": round(avg, 2), "calls": calls, "traffic_bytes": tb,
+        table[k] = {"avg_us": round(avg, 2), "timed_avg_us": round(timed.get(k, avg), 2),
+                    "calls": calls, "traffic_bytes": tb,
                     "fetch_kib_raw": fk, "write_kib_raw": wk, "mfma_busy": util, "l2_hit": hit}
-        rows.append("| %s | %d | %.1f | %.1f | %.1f | %s | %s | %s | %s |" % (
-            k, calls, avg, mn, mx,
+        rows.append("| %s | %d | %.1f | %.1f | %.1f | %.1f | %s | %s | %s | %s |" % (
+            k, calls, avg, timed.get(k, avg), mn, mx,
             "%.0f" % fk if fk is not None else "-", "%.0f" % wk if wk is not None else "-",
             "%.3f" % (tb / 1e9) if tb is not None else "-",
             ("%.2f / %.2f" % (util, hit)) if util is not None and hit is not None else "-"))
@@ -231,10 +249,13 @@ def summarize(prof_dir, out_path, workload, cmd):
         "",
         "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
         "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS). Counter runs serialize kernels, so their "
-        "durations are not used; the times come from the kernel-trace run.", "",
-        "| kernel | calls | avg us | min us | max us | FETCH_SIZE KiB | WRITE_SIZE KiB | "
-        "traffic GB | MFMA busy / L2 hit |",
-        "|---|---|---|---|---|---|---|---|---|",
+        "durations are not used; the times come from the kernel-trace run: `avg us` is "
+        "rocprofv3's average over every dispatch, `timed-step avg us` the average over the "
+        "dispatches of the timed steps (the warm-up step's left out), the figure to compare with "
+        "the bench line's stage times.", "",
+        "| kernel | calls | avg us | timed-step avg us | min us | max us | FETCH_SIZE KiB | "
+        "WRITE_SIZE KiB | traffic GB | MFMA busy / L2 hit |",
+        "|---|---|---|---|---|---|---|---|---|---|",
         *rows, "",
         "Source digest of the kernels profiled (sha256 of the csrc files, first 16 hex digits): "
         "`%s`" % meta["source_digest"], "",
