@@ -79,35 +79,15 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wsum) {
   return v + add;
 }
 
-__global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int32_t* status,
-                                                    int32_t* counts, int32_t* offsets,
-                                                    int32_t* blkhist, const int32_t* blkbad,
-                                                    int32_t* lpt, int32_t* src, int32_t* mt64,
-                                                    int32_t* mt128, int32_t* mt256) {
-  __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
-  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
-  __shared__ int32_t wsum[16];
+// The part of the scan kernel after the per-expert counts (every thread of the 1024 calls it;
+// thread e < E holds cnt = counts[e], every thread a partial count badp of out-of-range ids): counts, offsets (also left in s_off[0..E]), the three
+// row-tile lists, the longest-first expert order, src = -1 past the last routed row, the status.
+__device__ void plan_finish(int N, int E, int cnt, int badp, int32_t* s_cnt, int32_t* s_off,
+                            int32_t* wsum, int32_t* status, int32_t* counts, int32_t* offsets,
+                            int32_t* lpt, int32_t* src, int32_t* mt64, int32_t* mt128,
+                            int32_t* mt256) {
   const int tid = threadIdx.x;
-
-  // chunk bases within each expert (exclusive scan over chunks, in place) and the counts
-  // (the counts of a batch of chunks are loaded before any of them is overwritten, so the loads
-  // of a batch are in flight together)
-  int cnt = 0;
-  if (tid < E) {
-    constexpr int kBatch = 32;
-    int32_t* row = blkhist + (int64_t)tid * NB;
-    for (int b0 = 0; b0 < NB; b0 += kBatch) {
-      int v[kBatch];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) v[q] = b0 + q < NB ? row[b0 + q] : 0;
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        if (b0 + q < NB) row[b0 + q] = cnt;
-        cnt += v[q];
-      }
-    }
-    counts[tid] = cnt;
-  }
+  if (tid < E) counts[tid] = cnt;
   s_cnt[tid] = cnt;
   const int incl = block_scan_1024(cnt, wsum);
   s_off[tid] = incl - cnt;
@@ -144,13 +124,69 @@ __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int3
   // rows past the last routed row have no source slot
   for (int r = nvalid + tid; r < N; r += 1024) src[r] = -1;
 
-  // out-of-range total: per-thread partial sums over the chunks, then one scan
-  int badp = 0;
-  for (int b = tid; b < NB; b += 1024) badp += blkbad[b];
   const int bad = block_scan_1024(badp, wsum);
   if (tid == 1023) status[0] = bad;
   if (tid == 0)
     for (int w = 1 + kNumTileSizes; w < kStatusWords; ++w) status[w] = 0;
+}
+
+__global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int32_t* status,
+                                                    int32_t* counts, int32_t* offsets,
+                                                    int32_t* blkhist, const int32_t* blkbad,
+                                                    int32_t* lpt, int32_t* src, int32_t* mt64,
+                                                    int32_t* mt128, int32_t* mt256) {
+  __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x;
+
+  // chunk bases within each expert (exclusive scan over chunks, in place) and the counts
+  // (the counts of a batch of chunks are loaded before any of them is overwritten, so the loads
+  // of a batch are in flight together)
+  int cnt = 0;
+  if (tid < E) {
+    constexpr int kBatch = 32;
+    int32_t* row = blkhist + (int64_t)tid * NB;
+    for (int b0 = 0; b0 < NB; b0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) v[q] = b0 + q < NB ? row[b0 + q] : 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (b0 + q < NB) row[b0 + q] = cnt;
+        cnt += v[q];
+      }
+    }
+  }
+  // out-of-range total: per-thread partial sums over the chunks
+  int badp = 0;
+  for (int b = tid; b < NB; b += 1024) badp += blkbad[b];
+  plan_finish(N, E, cnt, badp, s_cnt, s_off, wsum, status, counts, offsets, lpt, src, mt64,
+              mt128, mt256);
+}
+
+// Orders a wavefront's LDS accesses before and after it, across its lanes (every lane's base
+// reads before the leaders' base updates, and those before the next group's reads), without
+// waiting for the wavefront's global stores.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Lanes of a wavefront holding the same expert id (ok lanes only) find each other with one ballot
+// per id bit; returns the lane's rank among its peers (lane order) and their number.
+__device__ __forceinline__ void peer_rank(bool ok, int v, int nbits, int& rank, int& cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t peers = __ballot(ok);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool one = ((v >> bit) & 1) != 0;
+    const uint64_t m = __ballot(ok && one);
+    peers &= one ? m : ~m;
+  }
+  rank = __popcll(peers & below);
+  cnt = __popcll(peers);
 }
 
 template <typename IdT>
@@ -173,7 +209,6 @@ __global__ __launch_bounds__(64) void moe_plan_scatter(const IdT* __restrict__ i
   }
   for (int e = lane; e < E; e += 64) base[e] = offsets[e] + blkhist[(int64_t)e * NB + b];
   __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int i0 = lo + 64 * q;
@@ -182,22 +217,15 @@ __global__ __launch_bounds__(64) void moe_plan_scatter(const IdT* __restrict__ i
     const bool in = i < hi;
     const int v = vv[q];
     const bool ok = v >= 0;
-    // lanes holding the same expert id: agree on every bit of the id
-    uint64_t peers = __ballot(ok);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool one = ((v >> bit) & 1) != 0;
-      const uint64_t m = __ballot(ok && one);
-      peers &= one ? m : ~m;
-    }
-    const int rank = __popcll(peers & below);
-    const int cnt = __popcll(peers);
+    int rank, cnt;
+    peer_rank(ok, v, nbits, rank, cnt);
     int p = -1;
     if (ok) p = base[v] + rank;
-    __syncthreads();
+    lds_wave_sync();  // the workgroup is this one wavefront
     if (in) pos[i] = p;
     if (ok) src[p] = i;
     if (ok && rank == 0) base[v] += cnt;
-    __syncthreads();
+    lds_wave_sync();
   }
 }
 
