@@ -3,7 +3,7 @@ include/moe_routed.h). Argument marshalling only: every step of the layer runs i
 HIP kernels. The functions keep the C names; tensors are passed as torch tensors (their device
 pointers are used), raw integer addresses or None.
 
-The library must be built (``python -m mixture_experts_routed_plan_amd.build``); importing this
+The library must be built (``python mixture_experts_routed_plan_amd/build.py``); importing this
 package without it raises ImportError -- there is no fallback implementation.
 """
 from __future__ import annotations
@@ -80,7 +80,7 @@ def _hip_runtimes():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("%s is not built; run `python -m mixture_experts_routed_plan_amd.build`"
+        raise ImportError("%s is not built; run `python mixture_experts_routed_plan_amd/build.py`"
                           % LIB_PATH)
     # The library and torch must share one HIP runtime: torch's streams and allocations belong to
     # the runtime torch loaded, and torch ships its own copy of the HIP and HSA runtimes. With

@@ -1,6 +1,6 @@
 """Build libmoe_routed.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m mixture_experts_routed_plan_amd.build
+    python mixture_experts_routed_plan_amd/build.py
 
 Every source under csrc/ is compiled to an object under _build/ and linked into
 mixture_experts_routed_plan_amd/libmoe_routed.so. Always recompiles.
