@@ -333,7 +333,32 @@ def extras(args, w, dv, M, x, scores, w13, w2, ids, stream, hip):
               "frac_peak": round(r_bytes / r_ms / 1e6 / PEAK_HBM_GBS, 4),
               "config": "softmax top-%d of %d, renormalised, %d tokens" % (w.K, w.E, w.T)}
 
-    return forward_only, router
+    # context, not a step of the path: the vendor library's dense bf16 GEMM (torch.matmul, which
+    # runs hipBLASLt) on the forward GEMMs' total work as one dense product each -- [N,D]x[D,2F]
+    # and [N,F]x[F,D] -- the practical MFMA ceiling of this GPU for these shapes
+    vendor = {}
+    for name, (m, kd, n) in (("w13", (w.N, w.D, 2 * w.F)), ("w2", (w.N, w.F, w.D))):
+        g.manual_seed(1)
+        a = torch.randn(m, kd, device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn(kd, n, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        for _ in range(2):
+            torch.matmul(a, b)
+        v0, v1 = hip.create(), hip.create()
+        torch.cuda.synchronize()
+        hip.record(v0, torch.cuda.current_stream().cuda_stream)
+        for _ in range(5):
+            torch.matmul(a, b)
+        hip.record(v1, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        v_ms = hip.ms(v0, v1) / 5
+        vendor[name] = {"ms": round(v_ms, 4),
+                        "tflops": round(2.0 * m * kd * n / (v_ms / 1e3) / 1e12, 1),
+                        "shape": [m, kd, n]}
+        del a, b
+    vendor["note"] = ("torch.matmul (hipBLASLt) on one dense bf16 GEMM of the same FLOPs as each "
+                      "forward grouped GEMM (M, K, N); no routing, gather or epilogue")
+
+    return forward_only, router, vendor
 
 
 def main():
@@ -494,9 +519,9 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
-    forward_only = router = None
+    forward_only = router = vendor = None
     if not args.skip_extras:
-        forward_only, router = extras(args, w, dv, M_lib(), x, scores, w13, w2, ids, stream, hip)
+        forward_only, router, vendor = extras(args, w, dv, M_lib(), x, scores, w13, w2, ids, stream, hip)
 
     flops = 18 * w.N * w.D * w.F
     res = {
@@ -523,6 +548,7 @@ def main():
         "stages": stages,
         "router": router,
         "forward_only": forward_only,
+        "vendor_dense_gemm": vendor,
     }
     hip.close()
     if args.cpu_baseline_tokens > 0:
