@@ -372,13 +372,39 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
   auto addrP = [&](int b) { return lds0 + (uint32_t)(b * (BM + BN) * BK * 2); };
   auto addrQ = [&](int b) { return lds0 + (uint32_t)((b * (BM + BN) * BK + BM * BK) * 2); };
 
+  // this wavefront's 32-row blocks (jlim of FM) and 32-column blocks (ilim of FN; for the SwiGLU
+  // forward per gate/up half) that hold any output: the products of the others (the ragged last
+  // row tile of an expert, a column tail) are skipped
+  const int tile_rows = t.r_lim - t.r0;
+  const int nblk = tile_rows >= BM ? BM / 32 : (tile_rows + 31) / 32;  // 32-row blocks with rows
+  const int jlim = nblk <= wr ? 0 : min(FM, (nblk - wr + WR - 1) / WR);
+  int ilim;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    const int cols_left = g.F - (t.n0 + wc * (WN / 2));
+    ilim = cols_left <= 0 ? 0 : (cols_left >= WN / 2 ? FN / 2 : (cols_left + 31) / 32);
+  } else {
+    const int cols_left = g.N_out - (t.n0 + wc * WN);
+    ilim = cols_left <= 0 ? 0 : (cols_left >= WN ? FN : (cols_left + 31) / 32);
+  }
+  // P copies of a row-ragged tile: wavefront w copies the tile's 32-row block w (rows
+  // 32w..32w+31, DmaTile with R = 256), so in a partly filled tile (an expert's ragged last row
+  // tile) the wavefronts whose block holds no row copy nothing; those LDS rows feed only the
+  // fragments of empty blocks, whose products are skipped (the fragment reads stay: skipping
+  // them costs registers)
+  static_assert(SCHED != SCHED_ROWS || (P_KC && DmaTile<BM>::NB * 8 * kWaves == BM && BM == 256),
+                "row-ragged GEMMs copy one 32-row block of P per wavefront");
+  const bool p_copy_on = SCHED != SCHED_ROWS || wave < nblk;
   // copy of one stage: NBO DMA blocks per operand and wavefront
   constexpr int NBO = DmaTile<BM>::NB, NC = 2 * NBO;
   static_assert(DmaTile<BM>::NB == MnTile<BM>::NB && DmaTile<BN>::NB == NBO, "copies per operand");
   auto copy_issue = [&](int b, int kt, int n) {
     const int k0 = kt * BK;  // relative to kbeg
     if (n < NBO) {
-      if constexpr (P_KC) pd.issue(addrP(b), t.kbeg + k0, n); else pm.issue(addrP(b), k0, klen, n);
+      if constexpr (P_KC) {
+        if (p_copy_on) pd.issue(addrP(b), t.kbeg + k0, n);
+      } else {
+        pm.issue(addrP(b), k0, klen, n);
+      }
     } else {
       if constexpr (Q_KC) qd.issue(addrQ(b), t.kbeg + k0, n - NBO); else qm.issue(addrQ(b), k0, klen, n - NBO);
     }
@@ -439,20 +465,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
   //   ks = 3, m >= B0:     the read operations of sub-step 0 of the next stage
   // The buffer written during stage s was last read before the barrier of stage s-1.
   constexpr int B0 = MPK * 3 / 4;
-  // this wavefront's 32-row blocks (jlim of FM) and 32-column blocks (ilim of FN; for the SwiGLU
-  // forward per gate/up half) that hold any output: the products of the others (the ragged last
-  // row tile of an expert, a column tail) are skipped
-  const int tile_rows = t.r_lim - t.r0;
-  const int nblk = tile_rows >= BM ? BM / 32 : (tile_rows + 31) / 32;  // 32-row blocks with rows
-  const int jlim = nblk <= wr ? 0 : min(FM, (nblk - wr + WR - 1) / WR);
-  int ilim;
-  if constexpr (EPI == EPI_SWIGLU_FWD) {
-    const int cols_left = g.F - (t.n0 + wc * (WN / 2));
-    ilim = cols_left <= 0 ? 0 : (cols_left >= WN / 2 ? FN / 2 : (cols_left + 31) / 32);
-  } else {
-    const int cols_left = g.N_out - (t.n0 + wc * WN);
-    ilim = cols_left <= 0 ? 0 : (cols_left >= WN ? FN : (cols_left + 31) / 32);
-  }
   auto block_on = [&](int i, int j) {
     return (EPI == EPI_SWIGLU_FWD ? (i % (FN / 2)) < ilim : i < ilim) && j < jlim;
   };
