@@ -13,10 +13,19 @@ HEADER = os.path.join(ROOT, "include", "moe_routed.h")
 LIB = os.path.join(ROOT, "mixture_experts_routed_plan_amd", "libmoe_routed.so")
 
 
+def _load_build_script(root):
+    """The build script, loaded by path: the package itself refuses to import unbuilt."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_moe_build_test", os.path.join(root, "mixture_experts_routed_plan_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def _ensure_built():
     if not os.path.exists(LIB):
-        from mixture_experts_routed_plan_amd import build as b
-        b.build()
+        _load_build_script(ROOT).build()
 
 
 _ensure_built()
@@ -164,3 +173,21 @@ def test_one_hip_runtime_when_imported_before_torch():
             "r = M._hip_runtimes()\nassert len(r) == 1, r\n")
     r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 0, r.stderr
+
+
+def test_build_entry_point_works_in_a_checkout_without_the_library(tmp_path):
+    """__graft_entry__.build() on a tree that has sources only (no libmoe_routed.so, no oracle
+    library): it compiles both and imports the package."""
+    import shutil
+    for d in ("mixture_experts_routed_plan_amd", "include", "oracle"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "*.so.tmp*", "__pycache__"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    assert not (tmp_path / "mixture_experts_routed_plan_amd" / "libmoe_routed.so").exists()
+    code = ("import sys; sys.path.insert(0, %r); import __graft_entry__ as g; g.build(); "
+            "import mixture_experts_routed_plan_amd as M; assert M.LIB_PATH.startswith(%r); "
+            "print(M.moe_abi_version())" % (str(tmp_path), str(tmp_path)))
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert (tmp_path / "mixture_experts_routed_plan_amd" / "libmoe_routed.so").exists()
+    assert r.stdout.strip().splitlines()[-1] == str(M.moe_abi_version())
