@@ -96,7 +96,9 @@ extern "C" {
  * more; otherwise the GEMMs gather x's token rows through the plan. */
 #define MOE_KEEP_XG 16
 
-/* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64,
+/* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64 with
+ * 64 <= D, F <= 2^22 and one expert's gate/up block below 4 GiB (4*F*D <= 2^32 bytes: the GEMM
+ * copies address an expert's weight rows and a tile's activation rows by 32-bit byte offsets),
  * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
@@ -108,7 +110,7 @@ typedef struct moe_shape {
   int64_t E;         /* experts on this GPU */
   int64_t K;         /* routed slots per token */
   int32_t ids_dtype; /* MOE_IDS_I32 or MOE_IDS_I64 */
-  int32_t flags;     /* 0 or MOE_SAVE_FOR_BACKWARD */
+  int32_t flags;     /* 0 or an OR of the MOE_SAVE_FOR_BACKWARD ... MOE_KEEP_XG flags above */
 } moe_shape;
 
 typedef enum moe_status {

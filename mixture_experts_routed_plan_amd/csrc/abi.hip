@@ -19,7 +19,11 @@ moe_status check_shape(const moe_shape* s) {
   if (s->T < 1 || s->K < 1 || s->K > MOE_MAX_TOPK) return MOE_E_SHAPE;
   if (s->E < 1 || s->E > MOE_MAX_EXPERTS) return MOE_E_SHAPE;
   if (s->D < 64 || s->F < 64 || (s->D % 64) != 0 || (s->F % 64) != 0) return MOE_E_SHAPE;
-  if (s->D > (1 << 24) || s->F > (1 << 24)) return MOE_E_SHAPE;
+  // the GEMM copies take 32-bit byte offsets from a per-expert (weights) or per-tile (activation
+  // rows) base: (2F - 1) rows of 2D bytes of w13[e] (4FD <= 2^32), and 255 rows of up to 4F or 2D
+  // bytes of a 256-row tile (D, F <= 2^22)
+  if (s->D > (1 << 22) || s->F > (1 << 22)) return MOE_E_SHAPE;
+  if (4 * s->F * s->D > (int64_t(1) << 32)) return MOE_E_SHAPE;
   if (s->T > (int64_t)(INT32_MAX - 1) / s->K) return MOE_E_SHAPE;
   return MOE_OK;
 }

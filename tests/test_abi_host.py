@@ -83,12 +83,21 @@ def test_sizes_are_closed_forms_of_the_shape():
 
 
 @pytest.mark.parametrize("kw", [dict(T=0), dict(K=0), dict(K=65), dict(E=0), dict(E=1025),
-                                dict(D=100), dict(F=96), dict(D=32), dict(T=2 ** 30, K=4)])
+                                dict(D=100), dict(F=96), dict(D=32), dict(T=2 ** 30, K=4),
+                                dict(D=2 ** 22 + 64), dict(F=2 ** 22 + 64),
+                                dict(D=32768, F=32768 + 64), dict(D=2 ** 22, F=512)])
 def test_bad_shapes_rejected(kw):
     s = shape(**kw)
     assert M.moe_plan_bytes(s) == 0
     assert M.moe_workspace_bytes(s) == 0
     assert M.moe_plan(s, 256, 256, 0) == M.MOE_E_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(D=32768, F=32768), dict(D=2 ** 22, F=256),
+                                dict(D=64, F=2 ** 22)])
+def test_largest_widths_accepted(kw):
+    # at the bounds: one expert's gate/up block is exactly 4 GiB, or a width is 2^22
+    assert M.moe_plan_bytes(shape(**kw)) > 0
 
 
 def test_bad_dtype_and_flags_rejected():
