@@ -25,6 +25,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->D > (1 << 22) || s->F > (1 << 22)) return MOE_E_SHAPE;
   if (4 * s->F * s->D > (int64_t(1) << 32)) return MOE_E_SHAPE;
   if (s->T > (int64_t)(INT32_MAX - 1) / s->K) return MOE_E_SHAPE;
+  if (gemm_max_grid(*s) > INT32_MAX) return MOE_E_SHAPE;
   return MOE_OK;
 }
 

@@ -39,6 +39,7 @@
 //     places on one XCD (workgroup id mod 8) take 32 consecutive logical tiles, and logical tiles
 //     run 8 row tiles deep before the next column tiles, so concurrently running tiles of an XCD
 //     share operand panels in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -806,12 +807,24 @@ GemmArgs rows_args(const moe_shape& s, const PlanPtrs& p, int bm) {
   return g;
 }
 
-int rows_grid(const moe_shape& s, int bm, int ntn) {
+int64_t rows_grid64(const moe_shape& s, int bm, int64_t ntn) {
   const int64_t mt_max = ceil_div(s.T * s.K, bm) + s.E;
-  return (int)(mt_max * ntn);
+  return mt_max * ntn;
 }
 
+// callers have checked gemm_max_grid(s) <= INT32_MAX
+int rows_grid(const moe_shape& s, int bm, int ntn) { return (int)rows_grid64(s, bm, ntn); }
+
 }  // namespace
+
+int64_t gemm_max_grid(const moe_shape& s) {
+  const int64_t fprop_w13 = rows_grid64(s, kBM, ceil_div(s.F, kBN / 2));
+  const int64_t by_d = rows_grid64(s, kBM, ceil_div(s.D, kBN));  // W2 FPROP, W13 DGRAD
+  const int64_t w2_bwd = (int64_t)align_up((size_t)rows_grid64(s, kBM, ceil_div(s.F, kBN)), 8) +
+                         s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN);
+  const int64_t wgrad_w13 = s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN);
+  return std::max(std::max(fprop_w13, by_d), std::max(w2_bwd, wgrad_w13));
+}
 
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
                             const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,

@@ -185,6 +185,9 @@ hipError_t launch_route(const moe_shape& s, const moe_router& r, const float* lo
                         float* weights, hipStream_t st);
 
 // grouped GEMMs
+// the largest workgroup count of any grouped-GEMM launch for this shape (launch grids and tile
+// indices are 32-bit)
+int64_t gemm_max_grid(const moe_shape& s);
 // gather: xg is x[T,D] and the P rows are gathered through the plan's src (fused permute)
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
                             const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,

@@ -85,7 +85,8 @@ def test_sizes_are_closed_forms_of_the_shape():
 @pytest.mark.parametrize("kw", [dict(T=0), dict(K=0), dict(K=65), dict(E=0), dict(E=1025),
                                 dict(D=100), dict(F=96), dict(D=32), dict(T=2 ** 30, K=4),
                                 dict(D=2 ** 22 + 64), dict(F=2 ** 22 + 64),
-                                dict(D=32768, F=32768 + 64), dict(D=2 ** 22, F=512)])
+                                dict(D=32768, F=32768 + 64), dict(D=2 ** 22, F=512),
+                                dict(T=2 ** 24, K=64, D=2 ** 20, F=1024)])
 def test_bad_shapes_rejected(kw):
     s = shape(**kw)
     assert M.moe_plan_bytes(s) == 0
