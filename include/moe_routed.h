@@ -99,7 +99,7 @@ extern "C" {
 /* Limits checked on the host: 1 <= E <= MOE_MAX_EXPERTS, D and F multiples of 64 with
  * 64 <= D, F <= 2^22 and one expert's gate/up block below 4 GiB (4*F*D <= 2^32 bytes: the GEMM
  * copies address an expert's weight rows and a tile's activation rows by 32-bit byte offsets),
- * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K < 2^31, and no grouped-GEMM launch above 2^31 - 1
+ * 1 <= K <= MOE_MAX_TOPK, T >= 1, T*K <= 2^31 - 2^16, and no grouped-GEMM launch above 2^31 - 1
  * workgroups (256 x 256 output tiles: about (T*K/256 + E) * max(D, 2F) / 256). */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64

@@ -24,7 +24,9 @@ moe_status check_shape(const moe_shape* s) {
   // bytes of a 256-row tile (D, F <= 2^22)
   if (s->D > (1 << 22) || s->F > (1 << 22)) return MOE_E_SHAPE;
   if (4 * s->F * s->D > (int64_t(1) << 32)) return MOE_E_SHAPE;
-  if (s->T > (int64_t)(INT32_MAX - 1) / s->K) return MOE_E_SHAPE;
+  // slot and row indices are 32-bit in the kernels, and the plan's last 1024-slot chunk must end
+  // below 2^31: at most 2^31 - 2^16 slots
+  if (s->T > ((int64_t(1) << 31) - (int64_t(1) << 16)) / s->K) return MOE_E_SHAPE;
   if (gemm_max_grid(*s) > INT32_MAX) return MOE_E_SHAPE;
   return MOE_OK;
 }

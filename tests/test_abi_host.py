@@ -86,7 +86,8 @@ def test_sizes_are_closed_forms_of_the_shape():
                                 dict(D=100), dict(F=96), dict(D=32), dict(T=2 ** 30, K=4),
                                 dict(D=2 ** 22 + 64), dict(F=2 ** 22 + 64),
                                 dict(D=32768, F=32768 + 64), dict(D=2 ** 22, F=512),
-                                dict(T=2 ** 24, K=64, D=2 ** 20, F=1024)])
+                                dict(T=2 ** 24, K=64, D=2 ** 20, F=1024),
+                                dict(T=2 ** 25 - 1023, K=64, D=64, F=64, E=1024)])
 def test_bad_shapes_rejected(kw):
     s = shape(**kw)
     assert M.moe_plan_bytes(s) == 0
@@ -95,7 +96,7 @@ def test_bad_shapes_rejected(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(D=32768, F=32768), dict(D=2 ** 22, F=256),
-                                dict(D=64, F=2 ** 22)])
+                                dict(D=64, F=2 ** 22), dict(T=2 ** 25 - 1024, K=64, D=64, F=64)])
 def test_largest_widths_accepted(kw):
     # at the bounds: one expert's gate/up block is exactly 4 GiB, or a width is 2^22
     assert M.moe_plan_bytes(shape(**kw)) > 0
