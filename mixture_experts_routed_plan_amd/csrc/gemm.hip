@@ -470,11 +470,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
     return (EPI == EPI_SWIGLU_FWD ? (i % (FN / 2)) < ilim : i < ilim) && j < jlim;
   };
   // one k stage; MASKED: skip the products of empty blocks (a tile with a ragged edge; full tiles
-  // run the unmasked copy of the body)
-  auto stage = [&](int kt, auto masked_tag) __attribute__((always_inline)) {
+  // run the unmasked copy of the body); MORE: a next stage exists (every stage but the last, which
+  // is peeled off so that the others carry no per-slot test of it)
+  auto stage = [&](int kt, auto masked_tag, auto more_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool more = decltype(more_tag)::value;
     const int cur = kt & 1, nxt = cur ^ 1;
-    const bool more = kt + 1 < nk;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       mask_tail(kt, ks);
@@ -515,9 +516,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
 #pragma unroll
     for (int n = 0; n < NR; ++n) read_op(0, 0, n);
     if (jlim == FM && ilim == (EPI == EPI_SWIGLU_FWD ? FN / 2 : FN)) {
-      for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{});
+      for (int kt = 0; kt < nk - 1; ++kt) stage(kt, std::false_type{}, std::true_type{});
+      stage(nk - 1, std::false_type{}, std::false_type{});
     } else {
-      for (int kt = 0; kt < nk; ++kt) stage(kt, std::true_type{});
+      for (int kt = 0; kt < nk - 1; ++kt) stage(kt, std::true_type{}, std::true_type{});
+      stage(nk - 1, std::true_type{}, std::false_type{});
     }
   }
 
