@@ -34,6 +34,12 @@
  *
  * Inputs may be bf16 bit patterns (uint16) or doubles (in_dtype); every intermediate and output is
  * an array of doubles (bf16-representable values when round_bf16 = 1).
+ *
+ * Error scales (optional outputs, test infrastructure): for every output that is a sum of terms
+ * (out and dx over the K slots, dscores over D, dW13 and dW2 over an expert's rows), the
+ * root-sum-square of its terms, sqrt(sum term^2). It is not part of the layer; the parity tests use
+ * it as the size scale of a reduction whose terms cancel, since a one-ulp difference in a bf16
+ * operand moves a sum by at most 2^-7 of that term.
  */
 #include <math.h>
 #include <omp.h>
@@ -242,7 +248,7 @@ static void load_row(const oracle_shape* s, const void* p, int64_t row, double* 
  * out[T,D]; rows past the last routed row are zero. */
 int oracle_forward(const oracle_shape* s, const void* x, const int64_t* ids, const double* scores,
                    const void* w13, const void* w2, const int64_t* pos, const int64_t* src,
-                   double* xg, double* h13, double* a, double* y, double* out) {
+                   double* xg, double* h13, double* a, double* y, double* out, double* out_rss) {
   const int64_t T = s->T, D = s->D, F = s->F, K = s->K, N = T * K;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < N; ++r) {
@@ -262,12 +268,17 @@ int oracle_forward(const oracle_shape* s, const void* x, const int64_t* ids, con
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t d = 0; d < D; ++d) {
-      double acc = 0.0;
+      double acc = 0.0, sq = 0.0;
       for (int64_t k = 0; k < K; ++k) {
         const int64_t p = pos[t * K + k];
-        if (p >= 0) acc += scores[t * K + k] * y[p * D + d];
+        if (p >= 0) {
+          const double term = scores[t * K + k] * y[p * D + d];
+          acc += term;
+          sq += term * term;
+        }
       }
       out[t * D + d] = R(s, acc);
+      if (out_rss) out_rss[t * D + d] = sqrt(sq);
     }
   }
   return 0;
@@ -280,16 +291,22 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
                     const int64_t* pos, const int64_t* src, const double* xg, const double* h13,
                     const double* a, const double* y, double* dy, double* dscores, double* dh13,
                     double* dxg, double* dx, double* dw13, double* dw2, const double* dw13_init,
-                    const double* dw2_init) {
+                    const double* dw2_init, double* dscores_rss, double* dx_rss, double* dw13_rss,
+                    double* dw2_rss) {
   const int64_t T = s->T, D = s->D, F = s->F, E = s->E, K = s->K, N = T * K;
   /* dscores[t,k] = sum_d dout[t,d] * y[pos[t,k], d]; 0 for a dropped slot */
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < N; ++i) {
     const int64_t t = i / K, p = pos[i];
-    double acc = 0.0;
+    double acc = 0.0, sq = 0.0;
     if (p >= 0)
-      for (int64_t d = 0; d < D; ++d) acc += ld(dout, t * D + d, s->in_dtype) * y[p * D + d];
+      for (int64_t d = 0; d < D; ++d) {
+        const double term = ld(dout, t * D + d, s->in_dtype) * y[p * D + d];
+        acc += term;
+        sq += term * term;
+      }
     dscores[i] = acc;
+    if (dscores_rss) dscores_rss[i] = sqrt(sq);
   }
   /* per-row input gradients */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -313,32 +330,45 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
   for (int64_t e = 0; e < E; ++e)
     for (int64_t d = 0; d < D; ++d)
       for (int64_t f = 0; f < F; ++f) {
-        double acc = 0.0;
-        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) acc += dy[r * D + d] * a[r * F + f];
+        double acc = 0.0, sq = 0.0;
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+          const double term = dy[r * D + d] * a[r * F + f];
+          acc += term;
+          sq += term * term;
+        }
         const int64_t o = (e * D + d) * F + f;
         dw2[o] = RW(s, (dw2_init ? dw2_init[o] : 0.0) + acc);
+        if (dw2_rss) dw2_rss[o] = sqrt(sq);
       }
   /* dW13[e,j,d] = R(init + sum_{r in segment e} dh13[r,j] * xg[r,d]) */
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t e = 0; e < E; ++e)
     for (int64_t j = 0; j < 2 * F; ++j)
       for (int64_t d = 0; d < D; ++d) {
-        double acc = 0.0;
-        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r)
-          acc += dh13[r * 2 * F + j] * xg[r * D + d];
+        double acc = 0.0, sq = 0.0;
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+          const double term = dh13[r * 2 * F + j] * xg[r * D + d];
+          acc += term;
+          sq += term * term;
+        }
         const int64_t o = (e * 2 * F + j) * D + d;
         dw13[o] = RW(s, (dw13_init ? dw13_init[o] : 0.0) + acc);
+        if (dw13_rss) dw13_rss[o] = sqrt(sq);
       }
   /* dx[t,d] = R(sum_k dxg[pos[t,k], d]), k ascending */
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t)
     for (int64_t d = 0; d < D; ++d) {
-      double acc = 0.0;
+      double acc = 0.0, sq = 0.0;
       for (int64_t k = 0; k < K; ++k) {
         const int64_t p = pos[t * K + k];
-        if (p >= 0) acc += dxg[p * D + d];
+        if (p >= 0) {
+          acc += dxg[p * D + d];
+          sq += dxg[p * D + d] * dxg[p * D + d];
+        }
       }
       dx[t * D + d] = R(s, acc);
+      if (dx_rss) dx_rss[t * D + d] = sqrt(sq);
     }
   return 0;
 }
@@ -351,7 +381,8 @@ int oracle_backward(const oracle_shape* s, const void* dout, const int64_t* ids,
  * rows' y (zero for a dropped slot). */
 int oracle_tokens(const oracle_shape* s, const void* x, const int64_t* ids, const double* scores,
                   const void* w13, const void* w2, const void* dout, int64_t n, const int64_t* toks,
-                  double* out_rows, double* dscore_rows, double* dx_rows, double* y_rows) {
+                  double* out_rows, double* dscore_rows, double* dx_rows, double* y_rows,
+                  double* out_rss, double* dscore_rss, double* dx_rss) {
   const int64_t D = s->D, F = s->F, K = s->K, E = s->E;
   int status = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -372,33 +403,47 @@ int oracle_tokens(const oracle_shape* s, const void* x, const int64_t* ids, cons
       row_forward(s, w13, w2, e, xrow, h + k * 2 * F, a, y + k * D);
     }
     for (int64_t d = 0; d < D; ++d) {
-      double acc = 0.0;
+      double acc = 0.0, sq = 0.0;
       for (int64_t k = 0; k < K; ++k) {
         const int64_t e = ids[t * K + k];
-        if (e >= 0 && e < E) acc += scores[t * K + k] * y[k * D + d];
+        if (e >= 0 && e < E) {
+          const double term = scores[t * K + k] * y[k * D + d];
+          acc += term;
+          sq += term * term;
+        }
       }
       out_rows[q * D + d] = R(s, acc);
+      if (out_rss) out_rss[q * D + d] = sqrt(sq);
     }
     if (y_rows) memcpy(y_rows + q * K * D, y, sizeof(double) * K * D);
     if (dout) {
       load_row(s, dout, t, drow);
       for (int64_t k = 0; k < K; ++k) {
         const int64_t e = ids[t * K + k];
-        double acc = 0.0;
+        double acc = 0.0, sq = 0.0;
         if (e >= 0 && e < E) {
-          for (int64_t d = 0; d < D; ++d) acc += drow[d] * y[k * D + d];
+          for (int64_t d = 0; d < D; ++d) {
+            const double term = drow[d] * y[k * D + d];
+            acc += term;
+            sq += term * term;
+          }
           row_backward(s, w13, w2, e, scores[t * K + k], drow, h + k * 2 * F, dy, dh,
                        dxg + k * D);
         }
         dscore_rows[q * K + k] = acc;
+        if (dscore_rss) dscore_rss[q * K + k] = sqrt(sq);
       }
       for (int64_t d = 0; d < D; ++d) {
-        double acc = 0.0;
+        double acc = 0.0, sq = 0.0;
         for (int64_t k = 0; k < K; ++k) {
           const int64_t e = ids[t * K + k];
-          if (e >= 0 && e < E) acc += dxg[k * D + d];
+          if (e >= 0 && e < E) {
+            acc += dxg[k * D + d];
+            sq += dxg[k * D + d] * dxg[k * D + d];
+          }
         }
         dx_rows[q * D + d] = R(s, acc);
+        if (dx_rss) dx_rss[q * D + d] = sqrt(sq);
       }
     }
     free(xrow); free(h); free(a); free(y); free(drow); free(dy); free(dh); free(dxg);
@@ -466,6 +511,30 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
   }
   free(fl);
   return 0;
+}
+
+/* Element-wise steps over arrays, for the whole-expert evaluation in oracle/__init__.py (which
+ * forms the expert's contractions with a library matmul): the same rounding, SwiGLU and SwiGLU
+ * derivative as the row functions above.
+ *   oracle_store_array: out[i] = R(v[i]), or RW(v[i]) when wgrad is set (weight-gradient storage);
+ *   oracle_swiglu_array: a[i] = R(silu(g[i]) * u[i]);
+ *   oracle_swiglu_grad_array: dg[i], du[i] from da[i], g[i], u[i] as swiglu_grad. */
+void oracle_store_array(const oracle_shape* s, int64_t n, int32_t wgrad, const double* v,
+                        double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = wgrad ? RW(s, v[i]) : R(s, v[i]);
+}
+
+void oracle_swiglu_array(const oracle_shape* s, int64_t n, const double* g, const double* u,
+                         double* a) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) a[i] = act_elem(s, g[i], u[i]);
+}
+
+void oracle_swiglu_grad_array(const oracle_shape* s, int64_t n, const double* da, const double* g,
+                              const double* u, double* dg, double* du) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) swiglu_grad(s, da[i], g[i], u[i], &dg[i], &du[i]);
 }
 
 /* ------------------------------------------------------------------------------------------- */

@@ -442,3 +442,100 @@ def test_sampled_wgrad_entries_follow_the_storage_mode():
     np.testing.assert_allclose(v13, i13 + full["dw13"][e].reshape(2 * w.F, w.D)[jd[:, 0], jd[:, 1]],
                                rtol=0, atol=1e-12)
     np.testing.assert_allclose(v2, i2 + full["dw2"][e][df[:, 0], df[:, 1]], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# whole weight gradients of one expert (the large-workload check of 4 experts' gradients)
+
+@pytest.mark.parametrize("name", ["p_skew", "p_ragged"])
+def test_expert_wgrad_is_the_full_evaluation(name):
+    """Every expert, the empty one included: bitwise the full evaluation's dW13[e], dW2[e] (bf16
+    storage); in fp32 storage and with accumulation onto existing gradients to the last bits of a
+    double; the root-sum-square scales to the last bits of a double."""
+    w = W.PARITY_WORKLOADS[name]
+    inp = W.make_inputs(w, router=oracle.route)
+    full = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, scales=True)
+    rng = np.random.default_rng(3)
+    i13 = _bf16_values(rng.standard_normal(full["dw13"].shape) * 0.1)
+    i2 = _bf16_values(rng.standard_normal(full["dw2"].shape) * 0.1)
+    f32 = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, wgrad_f32=True,
+                      dw13_init=i13, dw2_init=i2)
+    acc = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, dw13_init=i13,
+                      dw2_init=i2)
+    if name == "p_skew":
+        assert (full["counts"] == 0).any()
+    for e in range(w.E):
+        r = oracle.expert_wgrad(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e,
+                                scales=True)
+        np.testing.assert_array_equal(r["dw13"], full["dw13"][e])
+        np.testing.assert_array_equal(r["dw2"], full["dw2"][e])
+        for k in ("dw13_rss", "dw2_rss"):
+            np.testing.assert_allclose(r[k], full[k][e], rtol=1e-13, atol=0)
+        if full["counts"][e] == 0:
+            assert (r["dw13"] == 0).all() and (r["dw2"] == 0).all()
+        ra = oracle.expert_wgrad(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e,
+                                 init13=i13[e], init2=i2[e])
+        np.testing.assert_array_equal(ra["dw13"], acc["dw13"][e])
+        np.testing.assert_array_equal(ra["dw2"], acc["dw2"][e])
+        rf = oracle.expert_wgrad(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e,
+                                 wgrad_f32=True, init13=i13[e], init2=i2[e])
+        np.testing.assert_allclose(rf["dw13"], f32["dw13"][e], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(rf["dw2"], f32["dw2"][e], rtol=1e-13, atol=1e-15)
+
+
+def test_expert_wgrad_exact_mode_against_dense_autograd():
+    """float64 inputs, no rounding: the whole expert gradients against the dense torch autograd
+    brute force (every expert on every token, masked by the routing)."""
+    x, ids, s, w13, w2, dout = small_inputs(f64=True, dup=True, bad=True)
+    ref = dense_torch(x, ids, s, w13, w2, dout)
+    for e in range(w13.shape[0]):
+        r = oracle.expert_wgrad(x, ids, s, w13, w2, dout, e, mode="exact")
+        np.testing.assert_allclose(r["dw13"], ref["dw13"][e], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dw2"], ref["dw2"][e], rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# error scales: root-sum-square of a summed output's terms
+
+def test_error_scales_single_term_is_the_magnitude():
+    """A sum with one term: its root-sum-square is its magnitude (sqrt of a rounded square of a
+    double returns the magnitude exactly). One routed row per expert gives dW terms of one row;
+    K = 1 gives out and dx terms of one slot; a one-hot dout row gives one dscores term."""
+    T, D, F, E = 5, 64, 48, 5
+    x, _, s, w13, w2, dout = small_inputs(T=T, D=D, F=F, E=E, K=1, f64=True)
+    ids = np.arange(T, dtype=np.int64).reshape(T, 1)  # every expert has exactly one row
+    r = oracle.full(x, ids, s, w13, w2, dout, mode="exact", scales=True)
+    for k in ("out", "dx", "dw13", "dw2"):
+        np.testing.assert_array_equal(r[k + "_rss"], np.abs(r[k]))
+    oh = np.zeros_like(dout)
+    oh[np.arange(T), np.arange(T) * 3] = 1.5
+    r = oracle.full(x, ids, s, w13, w2, oh, mode="exact", scales=True)
+    np.testing.assert_array_equal(r["dscores_rss"], np.abs(r["dscores"]))
+    tk = oracle.tokens(x, ids, s, w13, w2, np.arange(T), oh, mode="exact", scales=True)
+    for k in ("out", "dscores", "dx"):
+        np.testing.assert_array_equal(tk[k + "_rss"], r[k + "_rss"])
+
+
+def test_error_scales_bound_the_sums_and_the_rounding_contract():
+    """Cauchy-Schwarz: |sum of n terms| <= sqrt(n) * rss; the bf16 contract, which rounds every
+    operand of every sum, stays within four bf16 ulps of the scale, 2^-5 * max(1, |exact|, rss),
+    of the exact layer for every summed output (measured: at most 2.2e-2 of it for dW13 on this
+    shape, 1.6e-2 for the others); scaling dout scales the backward's rss."""
+    inp = W.make_inputs(W.PARITY_WORKLOADS["p_skew"], router=oracle.route)
+    b = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, scales=True)
+    e = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="exact",
+                    scales=True)
+    w = inp.w
+    n_dw = np.maximum(b["counts"], 1)[:, None, None]
+    assert (np.abs(e["dw2"]) <= np.sqrt(n_dw) * e["dw2_rss"] * (1 + 1e-12)).all()
+    assert (np.abs(e["dw13"]).reshape(w.E, 2 * w.F, w.D)
+            <= np.sqrt(n_dw) * e["dw13_rss"].reshape(w.E, 2 * w.F, w.D) * (1 + 1e-12)).all()
+    assert (np.abs(e["dscores"]) <= math.sqrt(w.D) * e["dscores_rss"] * (1 + 1e-12)).all()
+    assert (np.abs(e["out"]) <= math.sqrt(w.K) * e["out_rss"] * (1 + 1e-12)).all()
+    for k in ("out", "dx", "dscores", "dw13", "dw2"):
+        tol = 2.0 ** -5 * np.maximum(np.maximum(1.0, np.abs(e[k])), e[k + "_rss"])
+        assert (np.abs(b[k] - e[k]) <= tol).all(), k
+    d2 = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, W.f32_to_bf16_bits(
+        2 * W.bf16_bits_to_f32(inp.dout)), mode="exact", scales=True)
+    for k in ("dscores_rss", "dx_rss", "dw13_rss", "dw2_rss"):
+        np.testing.assert_allclose(d2[k], 2 * e[k], rtol=1e-12, atol=0)
