@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import workloads as W
+from parity_check import check
 
 pytestmark = pytest.mark.gpu
 
@@ -73,13 +74,10 @@ def test_recompute_against_oracle():
     w = W.PARITY_WORKLOADS["p_ragged"]
     inp = W.make_inputs(w, with_dout=True, router=oracle.route)
     layer = _run(inp, True)
-    ref = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16")
-    for name, got in (("out", dv.bits_to_f64(dv.to_host_bits(layer.out))),
-                      ("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx))),
-                      ("dscores", layer.dscores.cpu().numpy().astype(np.float64)),
-                      ("dw13", dv.bits_to_f64(dv.to_host_bits(layer.dw13))),
-                      ("dw2", dv.bits_to_f64(dv.to_host_bits(layer.dw2)))):
-        r = ref[name]
-        err = float(np.abs(got - r).max()) / max(1.0, float(np.abs(r).max()))
-        log("  %-8s normwise %.3e" % (name, err))
-        assert err <= 2e-2, name
+    ref = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16",
+                      scales=True)
+    check("out", dv.bits_to_f64(dv.to_host_bits(layer.out)), ref["out"])
+    check("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx)), ref["dx"])
+    check("dscores", layer.dscores.cpu().numpy(), ref["dscores"], ref["dscores_rss"])
+    check("dw13", dv.bits_to_f64(dv.to_host_bits(layer.dw13)), ref["dw13"], ref["dw13_rss"])
+    check("dw2", dv.bits_to_f64(dv.to_host_bits(layer.dw2)), ref["dw2"], ref["dw2_rss"])

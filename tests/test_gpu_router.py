@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads as W
+from parity_check import check
 
 pytestmark = pytest.mark.gpu
 
@@ -119,11 +120,8 @@ def test_router_then_layer_matches_oracle():
     out = layer.forward(x, sc_d, w13, w2)
     layer.backward(dout, sc_d, w13, w2)
     torch.cuda.synchronize()
-    ref = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16")
-    for name, got, r in [("out", dv.bits_to_f64(dv.to_host_bits(out)), ref["out"]),
-                         ("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx)), ref["dx"]),
-                         ("dscores", layer.dscores.cpu().numpy().astype(np.float64),
-                          ref["dscores"])]:
-        err = float(np.abs(got - r).max()) / max(1.0, float(np.abs(r).max()))
-        log("  %-8s normwise %.3e" % (name, err))
-        assert err <= 2e-2, name
+    ref = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, mode="bf16",
+                      scales=True)
+    check("out", dv.bits_to_f64(dv.to_host_bits(out)), ref["out"])
+    check("dx", dv.bits_to_f64(dv.to_host_bits(layer.dx)), ref["dx"])
+    check("dscores", layer.dscores.cpu().numpy(), ref["dscores"], ref["dscores_rss"])
