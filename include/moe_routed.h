@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* moe_shape.ids_dtype */
 #define MOE_IDS_I32 0
@@ -122,7 +122,10 @@ typedef enum moe_status {
   MOE_E_DTYPE = -4,   /* ids_dtype or flags not recognised */
   MOE_E_HIP = -5,     /* a HIP launch or runtime call failed */
   MOE_E_BAD_IDS = -6, /* (moe_plan_status only) the routing held ids outside [0,E) */
-  MOE_E_STATE = -7    /* moe_backward on a shape without MOE_SAVE_FOR_BACKWARD */
+  MOE_E_STATE = -7,   /* moe_backward on a shape without MOE_SAVE_FOR_BACKWARD (moe_forward_noalloc:
+                         with it) */
+  MOE_E_SCRATCH = -8  /* (moe_forward_noalloc only) the shape needs more than
+                         MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status;
 
 /* Optional stage timing: when a non-NULL moe_trace is passed, the call records
@@ -174,6 +177,27 @@ moe_status moe_plan(const moe_shape* shape, const void* topk_ids, void* plan, hi
 moe_status moe_forward(const moe_shape* shape, const void* plan, const uint16_t* x,
                        const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
                        void* saved, void* workspace, hipStream_t stream, const moe_trace* trace);
+
+/* Allocation-free forward, for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation. It computes
+ * exactly what moe_forward computes without MOE_SAVE_FOR_BACKWARD (the same kernels, so the same
+ * bits), with the forward's intermediates (a[N,F], y[N,D], and xg[N,D] when materialized) kept in
+ * a scratch array that the library holds per GPU (MOE_NOALLOC_SCRATCH_BYTES, loaded with the
+ * library's code object and held until the process ends) instead of a caller workspace. The
+ * caller passes the inputs (plan from moe_plan, x, scores, w13, w2) and the output out, as for
+ * moe_forward. It calls no allocating routine; its first call on a GPU looks up that GPU's copy of
+ * the array (hipGetSymbolAddress). Nothing in the scratch has to start at zero: every element a
+ * call reads was written earlier in the same call, and each call overwrites what the last one
+ * left. Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Errors: as for moe_forward, plus MOE_E_STATE when the shape has MOE_SAVE_FOR_BACKWARD, and
+ * MOE_E_SCRATCH when the intermediates exceed MOE_NOALLOC_SCRATCH_BYTES: a and y take 2*N*F and
+ * 2*N*D bytes (each rounded up to 256), xg another 2*N*D when it is materialized (MOE_KEEP_XG, or
+ * x of 4 GiB or more). Both are host-side checks: nothing is enqueued. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* plan, const uint16_t* x,
+                               const float* scores, const uint16_t* w13, const uint16_t* w2,
+                               uint16_t* out, hipStream_t stream, const moe_trace* trace);
 
 /* Backward of moe_forward (Dist-MoE: DGRAD and WGRAD; MegaMoE "Design": the down projection's
  * weight gradient is produced before the gate/up one; here the gate/up weight gradient also runs

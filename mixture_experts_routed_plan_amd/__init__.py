@@ -36,6 +36,8 @@ MOE_E_DTYPE = -4
 MOE_E_HIP = -5
 MOE_E_BAD_IDS = -6
 MOE_E_STATE = -7
+MOE_E_SCRATCH = -8
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_shape(ctypes.Structure):
@@ -104,6 +106,7 @@ def _load():
         "moe_workspace_bytes": (ctypes.c_size_t, [S]),
         "moe_plan": (St, [S, P, P, P, Tr]),
         "moe_forward": (St, [S, P, P, P, P, P, P, P, P, P, Tr]),
+        "moe_forward_noalloc": (St, [S, P, P, P, P, P, P, P, Tr]),
         "moe_backward": (St, [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Tr]),
         "moe_plan_export": (St, [S, P, P, P, P, P, P]),
         "moe_plan_status": (St, [S, P, ctypes.POINTER(ctypes.c_int64), P]),
@@ -122,7 +125,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_plan_bytes", "moe_saved_bytes", "moe_workspace_bytes", "moe_plan", "moe_forward",
-            "moe_backward", "moe_plan_export", "moe_plan_status", "moe_saved_views",
+            "moe_forward_noalloc", "moe_backward", "moe_plan_export", "moe_plan_status", "moe_saved_views",
             "moe_route", "moe_status_str", "moe_abi_version")
 
 
@@ -187,6 +190,12 @@ def moe_forward(shape, plan, x, scores, w13, w2, out, saved=None, workspace=None
     return _lib.moe_forward(ctypes.byref(shape), _ptr(plan), _ptr(x), _ptr(scores), _ptr(w13),
                             _ptr(w2), _ptr(out), _ptr(saved), _ptr(workspace), _stream(stream),
                             None if trace is None else ctypes.byref(trace))
+
+
+def moe_forward_noalloc(shape, plan, x, scores, w13, w2, out, stream=None, trace=None) -> int:
+    return _lib.moe_forward_noalloc(ctypes.byref(shape), _ptr(plan), _ptr(x), _ptr(scores),
+                                    _ptr(w13), _ptr(w2), _ptr(out), _stream(stream),
+                                    None if trace is None else ctypes.byref(trace))
 
 
 def moe_backward(shape, plan, saved, x, dout, scores, w13, w2, dx, dw13, dw2, dscores, workspace,

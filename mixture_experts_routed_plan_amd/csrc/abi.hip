@@ -2,6 +2,8 @@
 // sequence of each call. No call allocates, and only moe_plan_status waits for the stream.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -49,67 +51,11 @@ struct Tracer {
     if (_e != hipSuccess) return MOE_E_HIP;       \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-int moe_abi_version(void) { return MOE_ABI_VERSION; }
-
-const char* moe_status_str(int status) {
-  switch (status) {
-    case MOE_OK: return "ok";
-    case MOE_E_NULL: return "a required pointer is null";
-    case MOE_E_SHAPE: return "shape outside the supported limits";
-    case MOE_E_ALIGN: return "a pointer is not suitably aligned";
-    case MOE_E_DTYPE: return "ids dtype or flags not recognised";
-    case MOE_E_HIP: return "a HIP launch or runtime call failed";
-    case MOE_E_BAD_IDS: return "routing held expert ids outside [0, E)";
-    case MOE_E_STATE: return "backward needs a shape with MOE_SAVE_FOR_BACKWARD";
-    default: return "unknown status";
-  }
-}
-
-size_t moe_plan_bytes(const moe_shape* s) {
-  if (check_shape(s) != MOE_OK) return 0;
-  return plan_layout(*s).total;
-}
-
-size_t moe_saved_bytes(const moe_shape* s) {
-  if (check_shape(s) != MOE_OK) return 0;
-  if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return 0;
-  return saved_layout(*s).total;
-}
-
-size_t moe_workspace_bytes(const moe_shape* s) {
-  if (check_shape(s) != MOE_OK) return 0;
-  return work_layout(*s).total;
-}
-
-moe_status moe_plan(const moe_shape* s, const void* topk_ids, void* plan, hipStream_t stream,
-                    const moe_trace* trace) {
-  moe_status st = check_shape(s);
-  if (st != MOE_OK) return st;
-  if (!topk_ids || !plan) return MOE_E_NULL;
-  if (!aligned(topk_ids, s->ids_dtype == MOE_IDS_I64 ? 8 : 4) || !aligned(plan, 16))
-    return MOE_E_ALIGN;
-  const PlanLayout L = plan_layout(*s);
-  const PlanPtrs p = plan_ptrs(L, plan);
-  Tracer tr{trace, stream, 0};
-  MOE_TRY(tr.mark());
-  MOE_TRY(launch_plan_hist(*s, L, p, topk_ids, stream));
-  MOE_TRY(tr.mark());
-  MOE_TRY(launch_plan_scan(*s, L, p, stream));
-  MOE_TRY(tr.mark());
-  MOE_TRY(launch_plan_scatter(*s, L, p, topk_ids, stream));
-  MOE_TRY(tr.mark());
-  return MOE_OK;
-}
-
-moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
-                       const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
-                       void* saved, void* workspace, hipStream_t stream, const moe_trace* trace) {
-  moe_status st = check_shape(s);
-  if (st != MOE_OK) return st;
+// The forward's launch sequence after check_shape (moe_forward and moe_forward_noalloc)
+moe_status forward_impl(const moe_shape* s, const void* plan, const uint16_t* x,
+                        const float* scores, const uint16_t* w13, const uint16_t* w2,
+                        uint16_t* out, void* saved, void* workspace, hipStream_t stream,
+                        const moe_trace* trace) {
   const bool save = (s->flags & MOE_SAVE_FOR_BACKWARD) != 0;
   const bool re = save && (s->flags & MOE_RECOMPUTE) != 0;
   if (!plan || !x || !scores || !w13 || !w2 || !out) return MOE_E_NULL;
@@ -158,6 +104,126 @@ moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
   MOE_TRY(launch_combine(*s, p.pos, y, scores, out, stream));
   MOE_TRY(tr.mark());
   return MOE_OK;
+}
+
+// ---- scratch of the allocation-free forward -------------------------------------------------
+// moe_forward_noalloc keeps the forward's intermediates (xg when materialized, a, y) in this
+// file-scope device array instead of a caller workspace: one copy per GPU, loaded with the code
+// object and held until the process ends. Its name is a host-side stand-in in host code, never a
+// device address: each device's address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Address of the device's copy of scratch for work on `stream` (its device; the current device for
+// the null stream).
+moe_status scratch_address(hipStream_t stream, void** addr) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_E_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return MOE_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MOE_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_E_HIP;
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_E_HIP;
+    if (e != hipSuccess || !a) return MOE_E_HIP;
+    g_scratch_addr[dev] = a;
+  }
+  *addr = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "a required pointer is null";
+    case MOE_E_SHAPE: return "shape outside the supported limits";
+    case MOE_E_ALIGN: return "a pointer is not suitably aligned";
+    case MOE_E_DTYPE: return "ids dtype or flags not recognised";
+    case MOE_E_HIP: return "a HIP launch or runtime call failed";
+    case MOE_E_BAD_IDS: return "routing held expert ids outside [0, E)";
+    case MOE_E_STATE: return "backward needs a shape with MOE_SAVE_FOR_BACKWARD";
+    case MOE_E_SCRATCH:
+      return "the shape needs more scratch than the allocation-free forward holds";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_plan_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return plan_layout(*s).total;
+}
+
+size_t moe_saved_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  if (!(s->flags & MOE_SAVE_FOR_BACKWARD)) return 0;
+  return saved_layout(*s).total;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return work_layout(*s).total;
+}
+
+moe_status moe_plan(const moe_shape* s, const void* topk_ids, void* plan, hipStream_t stream,
+                    const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !plan) return MOE_E_NULL;
+  if (!aligned(topk_ids, s->ids_dtype == MOE_IDS_I64 ? 8 : 4) || !aligned(plan, 16))
+    return MOE_E_ALIGN;
+  const PlanLayout L = plan_layout(*s);
+  const PlanPtrs p = plan_ptrs(L, plan);
+  Tracer tr{trace, stream, 0};
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_hist(*s, L, p, topk_ids, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_scan(*s, L, p, stream));
+  MOE_TRY(tr.mark());
+  MOE_TRY(launch_plan_scatter(*s, L, p, topk_ids, stream));
+  MOE_TRY(tr.mark());
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, const void* plan, const uint16_t* x,
+                       const float* scores, const uint16_t* w13, const uint16_t* w2, uint16_t* out,
+                       void* saved, void* workspace, hipStream_t stream, const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  return forward_impl(s, plan, x, scores, w13, w2, out, saved, workspace, stream, trace);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* s, const void* plan, const uint16_t* x,
+                               const float* scores, const uint16_t* w13, const uint16_t* w2,
+                               uint16_t* out, hipStream_t stream, const moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->flags & MOE_SAVE_FOR_BACKWARD) return MOE_E_STATE;
+  if (!plan || !x || !scores || !w13 || !w2 || !out) return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(out, 16) || !aligned(scores, 4))
+    return MOE_E_ALIGN;
+  if (work_layout(*s).fwd_total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_E_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(s, plan, x, scores, w13, w2, out, nullptr, ws, stream, trace);
 }
 
 moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,

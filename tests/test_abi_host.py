@@ -51,8 +51,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 3
-    for st in range(0, -8, -1):
+    assert M.moe_abi_version() == 4
+    for st in range(0, -9, -1):
         assert M.moe_status_str(st) != "unknown status"
     assert M.moe_status_str(-99) == "unknown status"
 
@@ -142,6 +142,25 @@ def test_null_and_alignment_rejected():
     assert M.moe_backward(s, a, a, a + 2, a, a, a, a, a, a, a, a, a, 0) == M.MOE_E_ALIGN  # x
     assert M.moe_plan_export(s, None, stream=0) == M.MOE_E_NULL
     assert M.moe_plan_status(s, None, 0)[0] == M.MOE_E_NULL
+
+
+def test_noalloc_forward_host_checks():
+    """The allocation-free forward rejects, before any HIP call: a shape that saves for the
+    backward, null or misaligned pointers, and a shape whose intermediates exceed its scratch."""
+    a = 4096
+    s = shape(save_for_backward=False)
+    assert M.moe_forward_noalloc(shape(), a, a, a, a, a, a, 0) == M.MOE_E_STATE
+    assert M.moe_forward_noalloc(s, a, a, a, a, a, None, 0) == M.MOE_E_NULL
+    assert M.moe_forward_noalloc(s, a, a + 8, a, a, a, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_forward_noalloc(s, a, a, a + 2, a, a, a, 0) == M.MOE_E_ALIGN
+    # a[N,F] and y[N,D] must fit: N = 16384 slots with D + F = 2048 is exactly 64 MiB (accepted:
+    # the GPU test runs it), one more token is not
+    assert 2 * 16384 * 2048 == M.MOE_NOALLOC_SCRATCH_BYTES
+    over = M.make_shape(8193, 1024, 1024, 8, 2, save_for_backward=False)
+    assert M.moe_forward_noalloc(over, a, a, a, a, a, a, 0) == M.MOE_E_SCRATCH
+    # materializing xg takes room too
+    keep = M.make_shape(8192, 1024, 1024, 8, 2, save_for_backward=False, keep_xg=True)
+    assert M.moe_forward_noalloc(keep, a, a, a, a, a, a, 0) == M.MOE_E_SCRATCH
 
 
 def test_router_arguments_rejected():
