@@ -287,6 +287,85 @@ def M_lib():
     return M
 
 
+def device_info(hip):
+    """The GPU's name, compute-unit count and peak engine clock as the runtime reports them."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    clk = ctypes.c_int()
+    hip.hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                              ctypes.c_int]
+    # hipDeviceAttributeClockRate (kHz)
+    ok = hip.hip.hipDeviceGetAttribute(ctypes.byref(clk), 5, 0) == 0
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "max_engine_clock_mhz": round(clk.value / 1e3) if ok else None}
+
+
+def spread(v):
+    """median, min, max and mean of a list of durations (ms)."""
+    import numpy as np
+    a = np.asarray(v, np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4), "mean": round(float(a.mean()), 4)}
+
+
+def plain_copy(dst, src):
+    dst.copy_(src)
+    return 0
+
+
+def hbm_evicted(w, M, layer, stream, hip, reps=20, evict_mib=1024):
+    """The HBM-bound row kernels launched alone through the C ABI, each launch preceded by a
+    read-only pass over a 1 GiB buffer (four times the 256 MB infinity cache, so no operand is
+    left in any cache), timed with HIP events around the kernel alone: median, min and max over
+    `reps` launches. A plain device copy of 1 GiB, also after an eviction pass, gives the
+    streaming ceiling of the same run."""
+    import torch
+    N, T, D, K = w.N, w.T, w.D, w.K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    rows = torch.randn(N, D, device="cuda", generator=g).to(torch.bfloat16)
+    tok = torch.randn(T, D, device="cuda", generator=g).to(torch.bfloat16)
+    sc = torch.rand(T, K, device="cuda", generator=g)
+    big_n = torch.empty(N, D, dtype=torch.bfloat16, device="cuda")
+    big_t = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    dsc = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    evict = torch.ones((evict_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    s, plan = layer.shape, layer.plan_buf
+    copy_src = torch.ones((evict_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    copy_dst = torch.empty_like(copy_src)
+    calls = {
+        "permute": (lambda: M.moe_permute(s, plan, tok, big_n, stream), 2 * T * D + 2 * N * D),
+        "combine": (lambda: M.moe_combine(s, plan, rows, sc, big_t, stream), 2 * N * D + 2 * T * D),
+        "dx_combine": (lambda: M.moe_combine(s, plan, rows, None, big_t, stream),
+                       2 * N * D + 2 * T * D),
+        "combine_bwd_dscores": (lambda: M.moe_combine_backward(s, plan, tok, rows, sc, big_n, dsc,
+                                                               stream), 2 * T * D + 4 * N * D),
+        "plain_copy_1gib": (lambda: plain_copy(copy_dst, copy_src), 2 * (evict_mib << 20)),
+    }
+    res = {}
+    cur = torch.cuda.current_stream()
+    for name, (fn, nbytes) in calls.items():
+        times = []
+        for _ in range(reps + 1):
+            torch.sum(evict, dim=0, out=sink)  # read-only eviction pass
+            e0, e1 = hip.create(), hip.create()
+            hip.record(e0, stream)
+            rc = fn()
+            if rc:
+                raise RuntimeError("%s: %s" % (name, M.moe_status_str(rc)))
+            hip.record(e1, stream)
+            cur.synchronize()
+            times.append(hip.ms(e0, e1))
+        sp = spread(times[1:])  # the first launch warms the code object
+        res[name] = dict(sp, gbs=round(nbytes / sp["median"] / 1e6, 1),
+                         frac_peak=round(nbytes / sp["median"] / 1e6 / PEAK_HBM_GBS, 4),
+                         algorithmic_bytes=nbytes)
+    del rows, tok, big_n, big_t, evict, copy_src, copy_dst
+    return res
+
+
 def extras(args, w, dv, M, x, scores, w13, w2, ids, stream, hip):
     """Forward-only timing (no saving: the permute is fused into the gate/up GEMM) and the
     router on this workload's token and expert counts."""
@@ -485,15 +564,19 @@ def main():
 
     names = PLAN_STAGES + FWD_STAGES + bwd_stages
     per = {n: [] for n in names}
+    step_ms = []
     for (tp, ep), (tf, ef), (tb, eb) in traces:
         for lst, evs in ((PLAN_STAGES, ep), (FWD_STAGES, ef), (bwd_stages, eb)):
             for i, n in enumerate(lst):
                 per[n].append(hip.ms(evs[i], evs[i + 1]))
+        step_ms.append(hip.ms(ep[0], eb[-1]))
     work = stage_work(w)
     stages = {}
     for n in names:
         avg = float(np.mean(per[n]))
-        ent = {"ms": round(avg, 4)}
+        sp = spread(per[n])
+        ent = {"ms": round(avg, 4), "median_ms": sp["median"], "min_ms": sp["min"],
+               "max_ms": sp["max"]}
         if n in empty:
             ent["note"] = empty[n]
         elif n in work:
@@ -519,9 +602,13 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = amount
 
-    forward_only = router = vendor = None
+    forward_only = router = vendor = evicted = None
     if not args.skip_extras:
         forward_only, router, vendor = extras(args, w, dv, M_lib(), x, scores, w13, w2, ids, stream, hip)
+        evicted = hbm_evicted(w, M_lib(), layer, stream, hip)
+        for n, ent in evicted.items():
+            if n in stages and "frac_peak" in stages[n]:
+                ent["in_step_frac_peak"] = stages[n]["frac_peak"]
 
     flops = 18 * w.N * w.D * w.F
     res = {
@@ -533,6 +620,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": spread(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -545,7 +633,9 @@ def main():
                    "keep_xg": args.keep_xg,
                    "parallelism": "single GPU (one EP rank's share)"},
         "roofline": roof,
+        "device": device_info(hip),
         "stages": stages,
+        "hbm_kernels_evicted": evicted,
         "router": router,
         "forward_only": forward_only,
         "vendor_dense_gemm": vendor,

@@ -223,6 +223,26 @@ moe_status moe_backward(const moe_shape* shape, const void* plan, const void* sa
                         float* dscores, void* workspace, hipStream_t stream,
                         const moe_trace* trace);
 
+/* The row steps on their own, for callers that run the expert GEMMs elsewhere or time the steps
+ * apart (TeraMoE README, worker list: dispatch writes the expert inputs, combine applies the
+ * weighted accumulation, gather reduces several results of one token locally; Dist-MoE
+ * "Understand the execution model": permute -> ... -> combine). Same kernels as inside
+ * moe_forward / moe_backward; plan from moe_plan with the same shape and ids; dropped slots
+ * (pos = -1) move nothing and add nothing.
+ *   moe_permute:          xg[pos[t*K+k]] = x[t]                  (xg [N,D] bf16, rows in grouped order)
+ *   moe_combine:          out[t] = bf16(sum_k w_k * rows[pos[t*K+k]]), k ascending in fp32, with
+ *                         w_k = scores[t,k], or 1 when scores is NULL (the dX reduction); rows [N,D]
+ *   moe_combine_backward: dy[pos[t*K+k]] = bf16(scores[t,k] * dout[t]);
+ *                         dscores[t,k] = sum_d dout[t,d] * y[pos[t*K+k], d] (fp32; 0 when dropped)
+ * Buffers 16-byte aligned (scores, dscores 4); errors as for moe_forward. */
+moe_status moe_permute(const moe_shape* shape, const void* plan, const uint16_t* x, uint16_t* xg,
+                       hipStream_t stream);
+moe_status moe_combine(const moe_shape* shape, const void* plan, const uint16_t* rows,
+                       const float* scores, uint16_t* out, hipStream_t stream);
+moe_status moe_combine_backward(const moe_shape* shape, const void* plan, const uint16_t* dout,
+                                const uint16_t* y, const float* scores, uint16_t* dy,
+                                float* dscores, hipStream_t stream);
+
 /* Copy the plan's integer arrays into caller device buffers (int32): counts[E], offsets[E+1],
  * pos[N], src[N] (src entries past the last routed row are -1). Any of them may be NULL. */
 moe_status moe_plan_export(const moe_shape* shape, const void* plan, int32_t* counts,

@@ -107,6 +107,9 @@ def _load():
         "moe_plan": (St, [S, P, P, P, Tr]),
         "moe_forward": (St, [S, P, P, P, P, P, P, P, P, P, Tr]),
         "moe_forward_noalloc": (St, [S, P, P, P, P, P, P, P, Tr]),
+        "moe_permute": (St, [S, P, P, P, P]),
+        "moe_combine": (St, [S, P, P, P, P, P]),
+        "moe_combine_backward": (St, [S, P, P, P, P, P, P, P]),
         "moe_backward": (St, [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Tr]),
         "moe_plan_export": (St, [S, P, P, P, P, P, P]),
         "moe_plan_status": (St, [S, P, ctypes.POINTER(ctypes.c_int64), P]),
@@ -125,7 +128,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_plan_bytes", "moe_saved_bytes", "moe_workspace_bytes", "moe_plan", "moe_forward",
-            "moe_forward_noalloc", "moe_backward", "moe_plan_export", "moe_plan_status", "moe_saved_views",
+            "moe_forward_noalloc", "moe_backward", "moe_permute", "moe_combine",
+            "moe_combine_backward", "moe_plan_export", "moe_plan_status", "moe_saved_views",
             "moe_route", "moe_status_str", "moe_abi_version")
 
 
@@ -196,6 +200,20 @@ def moe_forward_noalloc(shape, plan, x, scores, w13, w2, out, stream=None, trace
     return _lib.moe_forward_noalloc(ctypes.byref(shape), _ptr(plan), _ptr(x), _ptr(scores),
                                     _ptr(w13), _ptr(w2), _ptr(out), _stream(stream),
                                     None if trace is None else ctypes.byref(trace))
+
+
+def moe_permute(shape, plan, x, xg, stream=None) -> int:
+    return _lib.moe_permute(ctypes.byref(shape), _ptr(plan), _ptr(x), _ptr(xg), _stream(stream))
+
+
+def moe_combine(shape, plan, rows, scores, out, stream=None) -> int:
+    return _lib.moe_combine(ctypes.byref(shape), _ptr(plan), _ptr(rows), _ptr(scores), _ptr(out),
+                            _stream(stream))
+
+
+def moe_combine_backward(shape, plan, dout, y, scores, dy, dscores, stream=None) -> int:
+    return _lib.moe_combine_backward(ctypes.byref(shape), _ptr(plan), _ptr(dout), _ptr(y),
+                                     _ptr(scores), _ptr(dy), _ptr(dscores), _stream(stream))
 
 
 def moe_backward(shape, plan, saved, x, dout, scores, w13, w2, dx, dw13, dw2, dscores, workspace,

@@ -285,6 +285,44 @@ moe_status moe_backward(const moe_shape* s, const void* plan, const void* saved,
   return MOE_OK;
 }
 
+moe_status moe_permute(const moe_shape* s, const void* plan, const uint16_t* x, uint16_t* xg,
+                       hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!plan || !x || !xg) return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(xg, 16)) return MOE_E_ALIGN;
+  const PlanPtrs p = plan_ptrs(plan_layout(*s), (void*)plan);
+  MOE_TRY(launch_permute(*s, p.pos, x, xg, stream));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_shape* s, const void* plan, const uint16_t* rows,
+                       const float* scores, uint16_t* out, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!plan || !rows || !out) return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(rows, 16) || !aligned(out, 16) ||
+      (scores && !aligned(scores, 4)))
+    return MOE_E_ALIGN;
+  const PlanPtrs p = plan_ptrs(plan_layout(*s), (void*)plan);
+  MOE_TRY(launch_combine(*s, p.pos, rows, scores, out, stream));
+  return MOE_OK;
+}
+
+moe_status moe_combine_backward(const moe_shape* s, const void* plan, const uint16_t* dout,
+                                const uint16_t* y, const float* scores, uint16_t* dy,
+                                float* dscores, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!plan || !dout || !y || !scores || !dy || !dscores) return MOE_E_NULL;
+  if (!aligned(plan, 16) || !aligned(dout, 16) || !aligned(y, 16) || !aligned(dy, 16) ||
+      !aligned(scores, 4) || !aligned(dscores, 4))
+    return MOE_E_ALIGN;
+  const PlanPtrs p = plan_ptrs(plan_layout(*s), (void*)plan);
+  MOE_TRY(launch_combine_bwd(*s, p.pos, dout, y, scores, dy, dscores, stream));
+  return MOE_OK;
+}
+
 moe_status moe_route(const moe_shape* s, const moe_router* r, const float* logits,
                      void* topk_ids, float* scores, hipStream_t stream, const moe_trace* trace) {
   if (!s || !r) return MOE_E_NULL;

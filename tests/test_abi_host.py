@@ -163,6 +163,19 @@ def test_noalloc_forward_host_checks():
     assert M.moe_forward_noalloc(keep, a, a, a, a, a, a, 0) == M.MOE_E_SCRATCH
 
 
+def test_row_step_arguments_rejected():
+    a = 4096
+    s = shape()
+    assert M.moe_permute(s, a, None, a, 0) == M.MOE_E_NULL
+    assert M.moe_permute(s, a, a + 2, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_combine(s, a, a, a, None, 0) == M.MOE_E_NULL
+    assert M.moe_combine(s, a, a, a + 2, a, 0) == M.MOE_E_ALIGN  # scores
+    assert M.moe_combine(s, a, a + 8, None, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_combine_backward(s, a, a, a, None, a, a, 0) == M.MOE_E_NULL  # scores required
+    assert M.moe_combine_backward(s, a, a, a, a, a + 8, a, 0) == M.MOE_E_ALIGN
+    assert M.moe_combine(shape(T=0), a, a, a, a, 0) == M.MOE_E_SHAPE
+
+
 def test_router_arguments_rejected():
     a = 4096
     s = shape(E=16, K=4)
