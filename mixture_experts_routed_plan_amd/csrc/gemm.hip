@@ -37,8 +37,8 @@
 //     no rows writes zeros. One workgroup owns each output tile: no atomics, no split-K.
 //   * XCD-aware order: within each window of 256 consecutive workgroups, the 32 that the hardware
 //     places on one XCD (workgroup id mod 8) take 32 consecutive logical tiles, and logical tiles
-//     run 8 row tiles deep before the next column tiles, so concurrently running tiles of an XCD
-//     share operand panels in that XCD's L2.
+//     run 8 row tiles deep (one expert's row tiles at a time) before the next column tiles, so
+//     concurrently running tiles of an XCD share operand panels in that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -129,14 +129,21 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t, int b) {
   const int L = b < full ? (b & ~255) + (b & 7) * 32 + ((b & 255) >> 3) : b;
   if (L >= total) return false;
   if (SCHED == SCHED_ROWS) {
-    const int mtc = g.mtile_count[0];
-    const int grp = L / (kGroupRows * ntn), within = L % (kGroupRows * ntn);
-    const int gm = min(kGroupRows, mtc - grp * kGroupRows);
-    const int mt = grp * kGroupRows + within % gm, nt = within / gm;
-    const int2 te = g.mtiles[mt];
-    t.e = te.x;
-    t.r0 = te.y;
-    t.r_lim = g.offsets[te.x + 1];
+    // an expert's row tiles are consecutive in the list, so the logical tiles of expert e are
+    // [ts*ntn, (ts+nt_e)*ntn) with ts its first row tile: L / ntn names a row tile of L's expert.
+    // Groups of kGroupRows row tiles are formed within each expert, so the tiles that run side by
+    // side on an XCD share one expert's weight panels
+    const int2 tq = g.mtiles[L / ntn];
+    const int e = tq.x, ebeg = g.offsets[e], eend = g.offsets[e + 1];
+    const int ts = L / ntn - (tq.y - ebeg) / BM;
+    const int nte = (eend - ebeg + BM - 1) / BM;
+    const int Le = L - ts * ntn;
+    const int grp = Le / (kGroupRows * ntn), within = Le % (kGroupRows * ntn);
+    const int gm = min(kGroupRows, nte - grp * kGroupRows);
+    const int mt = grp * kGroupRows + within % gm, nt = within / gm;  // row tile within e
+    t.e = e;
+    t.r0 = ebeg + mt * BM;
+    t.r_lim = eend;
     t.n0 = nt * (EPI == EPI_SWIGLU_FWD ? BN / 2 : BN);
     t.kbeg = 0;
     t.kend = g.Kdim;
