@@ -143,7 +143,9 @@ typedef struct moe_trace {
   hipEvent_t events[MOE_TRACE_MAX_EVENTS];
 } moe_trace;
 
-/* Byte sizes of the caller-allocated buffers; 0 for a shape that fails the checks. */
+/* Byte sizes of the caller-allocated buffers (Dist-MoE "Plan memory": the caller learns the
+ * device memory a configuration needs before it runs; here every size is a closed form of the
+ * shape, so no planner object is kept); 0 for a shape that fails the checks. */
 size_t moe_plan_bytes(const moe_shape* shape);
 size_t moe_saved_bytes(const moe_shape* shape);     /* 0 unless MOE_SAVE_FOR_BACKWARD */
 size_t moe_workspace_bytes(const moe_shape* shape); /* forward without save or with recompute,
@@ -244,16 +246,23 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* plan, const 
                                 float* dscores, hipStream_t stream);
 
 /* Copy the plan's integer arrays into caller device buffers (int32): counts[E], offsets[E+1],
- * pos[N], src[N] (src entries past the last routed row are -1). Any of them may be NULL. */
+ * pos[N], src[N] (src entries past the last routed row are -1). Any of them may be NULL.
+ * (Dist-MoE "Understand the execution model": the routing metadata built on the GPU drives the
+ * permute, the expert GEMMs and the combine; this exposes it to the caller, e.g. for a
+ * dispatcher that sends the grouped rows elsewhere.) Enqueued on stream; errors as for moe_plan. */
 moe_status moe_plan_export(const moe_shape* shape, const void* plan, int32_t* counts,
                            int32_t* offsets, int32_t* pos, int32_t* src, hipStream_t stream);
 
 /* Wait for the stream, then report the plan's status word: *bad_ids (host pointer, may be NULL)
- * receives the number of out-of-range ids; returns MOE_E_BAD_IDS when it is non-zero. */
+ * receives the number of out-of-range ids; returns MOE_E_BAD_IDS when it is non-zero.
+ * (Dist-MoE "BF16 Quickstart" and "Understand the execution model" require ids in [0,E) and trap
+ * on others; here such slots are dropped and counted, and this call reports the count.) The only
+ * call that waits for the stream. */
 moe_status moe_plan_status(const moe_shape* shape, const void* plan, int64_t* bad_ids,
                            hipStream_t stream);
 
-/* Device pointers to the saved forward intermediates inside saved (for inspection and tests):
+/* (TeraMoE README, activation-memory table: what the forward keeps for the backward.)
+ * Device pointers to the saved forward intermediates inside saved (for inspection and tests):
  * xg[N,D], h13[N,2F], a[N,F], y[N,D], all bf16. Any output pointer may be NULL. Intermediates that
  * are not saved come back as NULL: h13 and a with MOE_RECOMPUTE, xg unless MOE_KEEP_XG or x
  * spans 4 GiB or more (the GEMMs then read x through the plan). */
@@ -290,7 +299,10 @@ typedef struct moe_router {
 moe_status moe_route(const moe_shape* shape, const moe_router* router, const float* logits,
                      void* topk_ids, float* scores, hipStream_t stream, const moe_trace* trace);
 
+/* A fixed English description of a moe_status value ("unknown status" for others); static
+ * storage, never NULL. */
 const char* moe_status_str(int status);
+/* The version of this interface (the value of MOE_ABI_VERSION the library was built with). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus
