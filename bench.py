@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import re
 import os
 import sys
 import time
@@ -467,7 +468,9 @@ def main():
     if args.summarize:
         cmd_file = os.path.join(args.summarize[0], "commands.txt")
         cmd = open(cmd_file).read().strip().splitlines() if os.path.exists(cmd_file) else []
-        summarize(args.summarize[0], args.summarize[1], args.workload, cmd)
+        # the profiled command names its workload; it wins over --workload
+        named = [m.group(1) for line in cmd for m in [re.search(r"--workload (\w+)", line)] if m]
+        summarize(args.summarize[0], args.summarize[1], named[0] if named else args.workload, cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is one GPU's share of an "
