@@ -157,7 +157,7 @@ size_t moe_workspace_bytes(const moe_shape* shape); /* forward without save or w
  *   counts[e] = #slots routed to e;  offsets[e] = sum of counts below e;
  *   pos[i] = offsets[id_i] + #{j < i : id_j = id_i}  (stable expert-grouped row of slot i; -1 when
  *            id_i is out of range);  src[pos[i]] = i;
- *   the per-expert row-tile lists the grouped GEMMs walk, an expert order by decreasing count,
+ *   the row-tile list the grouped GEMMs walk, an expert order by decreasing count,
  *   and the status word (number of out-of-range ids). */
 moe_status moe_plan(const moe_shape* shape, const void* topk_ids, void* plan, hipStream_t stream,
                     const moe_trace* trace);

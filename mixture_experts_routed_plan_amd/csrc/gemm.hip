@@ -61,6 +61,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kEpWaveElems = 65536 / kWaves;  // per-wavefront epilogue staging area (bf16 elements)
 constexpr int kGroupRows = 8;
+static_assert(kRowTile % 32 == 0 && kRowTile <= kBM, "a plan row tile fits one output tile");
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
 // EPI_STORE output: bf16 (C), bf16 added to the existing values, fp32 (Cf), fp32 added
@@ -88,6 +89,7 @@ struct GemmArgs {
   int E;
   const int32_t* offsets;      // [E+1] expert row offsets
   const int2* mtiles;          // SCHED_ROWS: (expert, first row) per row tile
+  const int32_t* mtile_start;  // SCHED_ROWS: each expert's first index in mtiles
   const int32_t* mtile_count;  // SCHED_ROWS: number of row tiles (device)
   const int32_t* lpt;          // SCHED_KSEG: experts by decreasing row count
   // P rows gathered from token rows (fused permute): P row r is row src[r] / gather_k of P
@@ -132,18 +134,18 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t, int b) {
     // an expert's row tiles are consecutive in the list, so the logical tiles of expert e are
     // [ts*ntn, (ts+nt_e)*ntn) with ts its first row tile: L / ntn names a row tile of L's expert.
     // Groups of kGroupRows row tiles are formed within each expert, so the tiles that run side by
-    // side on an XCD share one expert's weight panels
-    const int2 tq = g.mtiles[L / ntn];
-    const int e = tq.x, ebeg = g.offsets[e], eend = g.offsets[e + 1];
-    const int ts = L / ntn - (tq.y - ebeg) / BM;
-    const int nte = (eend - ebeg + BM - 1) / BM;
+    // side on an XCD share one expert's weight panels. A tile ends where the expert's next tile
+    // starts (at most kRowTile <= BM rows)
+    const int e = g.mtiles[L / ntn].x, eend = g.offsets[e + 1];
+    const int ts = g.mtile_start[e];
+    const int nte = (eend - g.offsets[e] + kRowTile - 1) / kRowTile;
     const int Le = L - ts * ntn;
     const int grp = Le / (kGroupRows * ntn), within = Le % (kGroupRows * ntn);
     const int gm = min(kGroupRows, nte - grp * kGroupRows);
     const int mt = grp * kGroupRows + within % gm, nt = within / gm;  // row tile within e
     t.e = e;
-    t.r0 = ebeg + mt * BM;
-    t.r_lim = eend;
+    t.r0 = g.mtiles[ts + mt].y;
+    t.r_lim = mt + 1 < nte ? g.mtiles[ts + mt + 1].y : eend;
     t.n0 = nt * (EPI == EPI_SWIGLU_FWD ? BN / 2 : BN);
     t.kbeg = 0;
     t.kend = g.Kdim;
@@ -806,31 +808,32 @@ hipError_t launch(void (*kernel)(GemmArgs), const GemmArgs& g, int grid, hipStre
   return hipGetLastError();
 }
 
-GemmArgs rows_args(const moe_shape& s, const PlanPtrs& p, int bm) {
+GemmArgs rows_args(const moe_shape& s, const PlanPtrs& p) {
   GemmArgs g{};
   g.F = (int)s.F;
   g.E = (int)s.E;
   g.offsets = p.offsets;
-  const int ti = tile_size_index(bm);
-  g.mtiles = (const int2*)p.mtiles[ti];
-  g.mtile_count = p.status + 1 + ti;
+  g.mtiles = (const int2*)p.mtiles;
+  g.mtile_start = p.tstart;
+  g.mtile_count = p.status + 1;
   return g;
 }
 
-int64_t rows_grid64(const moe_shape& s, int bm, int64_t ntn) {
-  const int64_t mt_max = ceil_div(s.T * s.K, bm) + s.E;
+// the plan's worst-case row-tile count times the column tiles
+int64_t rows_grid64(const moe_shape& s, int64_t ntn) {
+  const int64_t mt_max = ceil_div(s.T * s.K, kRowTile) + s.E;
   return mt_max * ntn;
 }
 
 // callers have checked gemm_max_grid(s) <= INT32_MAX
-int rows_grid(const moe_shape& s, int bm, int ntn) { return (int)rows_grid64(s, bm, ntn); }
+int rows_grid(const moe_shape& s, int ntn) { return (int)rows_grid64(s, ntn); }
 
 }  // namespace
 
 int64_t gemm_max_grid(const moe_shape& s) {
-  const int64_t fprop_w13 = rows_grid64(s, kBM, ceil_div(s.F, kBN / 2));
-  const int64_t by_d = rows_grid64(s, kBM, ceil_div(s.D, kBN));  // W2 FPROP, W13 DGRAD
-  const int64_t w2_bwd = (int64_t)align_up((size_t)rows_grid64(s, kBM, ceil_div(s.F, kBN)), 8) +
+  const int64_t fprop_w13 = rows_grid64(s, ceil_div(s.F, kBN / 2));
+  const int64_t by_d = rows_grid64(s, ceil_div(s.D, kBN));  // W2 FPROP, W13 DGRAD
+  const int64_t w2_bwd = (int64_t)align_up((size_t)rows_grid64(s, ceil_div(s.F, kBN)), 8) +
                          s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN);
   const int64_t wgrad_w13 = s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN);
   return std::max(std::max(fprop_w13, by_d), std::max(w2_bwd, wgrad_w13));
@@ -839,7 +842,7 @@ int64_t gemm_max_grid(const moe_shape& s) {
 hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* xg,
                             const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,
                             bool gather) {
-  GemmArgs g = rows_args(s, p, kBM);
+  GemmArgs g = rows_args(s, p);
   g.P = xg; g.ldp = s.D;
   if (gather) {  // xg is x: P rows come from the routed rows' tokens
     g.gather_src = p.src;
@@ -850,23 +853,23 @@ hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
   g.C2 = a; g.ldc2 = s.F;
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
   const int ntn = (int)ceil_div(s.F, kBN / 2);
-  return launch(moe_fprop_w13_swiglu, g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_fprop_w13_swiglu, g, rows_grid(s, ntn), st);
 }
 
 hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
                            const uint16_t* w2, uint16_t* y, hipStream_t st) {
-  GemmArgs g = rows_args(s, p, kBM);
+  GemmArgs g = rows_args(s, p);
   g.P = a; g.ldp = s.F;
   g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F;
   g.C = y; g.ldc = s.D;
   g.N_out = (int)s.D; g.Kdim = (int)s.F;
   const int ntn = (int)ceil_div(s.D, kBN);
-  return launch(moe_fprop_w2, g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_fprop_w2, g, rows_grid(s, ntn), st);
 }
 
 static GemmArgs dgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
                               const uint16_t* w2, const uint16_t* h13, uint16_t* dh13) {
-  GemmArgs g = rows_args(s, p, kBM);
+  GemmArgs g = rows_args(s, p);
   g.P = dy; g.ldp = s.D;
   g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F;  // w2[e] read as [k = d][c = f]
   g.C = dh13; g.ldc = 2 * s.F;
@@ -889,7 +892,7 @@ static GemmArgs wgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint1
 hipError_t launch_w2_backward(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
                               const uint16_t* w2, const uint16_t* h13, uint16_t* dh13,
                               const uint16_t* a, void* dw2, hipStream_t st) {
-  const int grid_d = (int)align_up((size_t)rows_grid(s, kBM, (int)ceil_div(s.F, kBN)), 8);
+  const int grid_d = (int)align_up((size_t)rows_grid(s, (int)ceil_div(s.F, kBN)), 8);
   const int grid_w = (int)(s.E * ceil_div(s.D, kBM) * ceil_div(s.F, kBN));
   hipLaunchKernelGGL(w2_backward_kernel(s), dim3(grid_d + grid_w), dim3(kThreads), 0, st,
                      dgrad_w2_args(s, p, dy, w2, h13, dh13), wgrad_w2_args(s, p, dy, a, dw2),
@@ -899,13 +902,13 @@ hipError_t launch_w2_backward(const moe_shape& s, const PlanPtrs& p, const uint1
 
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st) {
-  GemmArgs g = rows_args(s, p, kBM);
+  GemmArgs g = rows_args(s, p);
   g.P = dh13; g.ldp = 2 * s.F;
   g.Q = w13; g.ldq = s.D; g.q_estride = 2 * s.F * s.D;  // w13[e] read as [k = j][c = d]
   g.C = dxg; g.ldc = s.D;
   g.N_out = (int)s.D; g.Kdim = (int)(2 * s.F);
   const int ntn = (int)ceil_div(s.D, kBN);
-  return launch(moe_dgrad_w13, g, rows_grid(s, kBM, ntn), st);
+  return launch(moe_dgrad_w13, g, rows_grid(s, ntn), st);
 }
 
 

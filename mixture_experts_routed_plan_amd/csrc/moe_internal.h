@@ -14,18 +14,19 @@ namespace moe {
 // sizes and layouts
 
 constexpr int kPlanChunk = 1024;  // slots per plan workgroup (a multiple of 64)
-constexpr int kNumTileSizes = 3;  // row-tile lists kept in the plan: 64, 128, 256 rows
-constexpr int kTileRows[kNumTileSizes] = {64, 128, 256};
-constexpr int kStatusWords = 16;  // [0] out-of-range ids, [1 + s] row tiles for kTileRows[s]
-
-inline int tile_size_index(int bm) { return bm == 64 ? 0 : (bm == 128 ? 1 : 2); }
+// Row tiles of the row-ragged GEMMs: an expert's rows in tiles of kRowTile (the last one holds
+// the rest). The plan lists (expert, first row) of every tile, experts ascending, and each
+// expert's first list index. (Splitting each expert's rows into equal tiles of 32-row multiples
+// instead measured the same at 256 rows and slower at 224 or 192.)
+constexpr int kRowTile = 256;
+constexpr int kStatusWords = 16;  // [0] out-of-range ids, [1] row tiles in the list
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct PlanLayout {
   int64_t N, E, NB;
-  size_t status, counts, offsets, pos, src, blkhist, blkbad, lpt, mtiles[kNumTileSizes], total;
+  size_t status, counts, offsets, pos, src, blkhist, blkbad, lpt, tstart, mtiles, total;
 };
 
 inline PlanLayout plan_layout(const moe_shape& s) {
@@ -47,8 +48,8 @@ inline PlanLayout plan_layout(const moe_shape& s) {
   L.blkhist = take(sizeof(int32_t) * L.E * L.NB);
   L.blkbad = take(sizeof(int32_t) * L.NB);
   L.lpt = take(sizeof(int32_t) * L.E);
-  for (int t = 0; t < kNumTileSizes; ++t)
-    L.mtiles[t] = take(sizeof(int32_t) * 2 * (ceil_div(L.N, kTileRows[t]) + L.E));
+  L.tstart = take(sizeof(int32_t) * L.E);
+  L.mtiles = take(sizeof(int32_t) * 2 * (ceil_div(L.N, kRowTile) + L.E));
   L.total = o;
   return L;
 }
@@ -146,7 +147,8 @@ struct PlanPtrs {
   int32_t* blkhist;
   int32_t* blkbad;
   int32_t* lpt;
-  int32_t* mtiles[kNumTileSizes];
+  int32_t* tstart;
+  int32_t* mtiles;
 };
 
 inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
@@ -160,7 +162,8 @@ inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
   p.blkhist = (int32_t*)(b + L.blkhist);
   p.blkbad = (int32_t*)(b + L.blkbad);
   p.lpt = (int32_t*)(b + L.lpt);
-  for (int t = 0; t < kNumTileSizes; ++t) p.mtiles[t] = (int32_t*)(b + L.mtiles[t]);
+  p.tstart = (int32_t*)(b + L.tstart);
+  p.mtiles = (int32_t*)(b + L.mtiles);
   return p;
 }
 

@@ -2,13 +2,14 @@
 //
 // Dist-MoE 0.1.0 (PyPI page), "Understand the execution model": the routing metadata is generated
 // on the GPU from the caller's expert ids. TeraMoE README, worker list: a scheduler forms
-// per-expert compute batches -- here the per-expert row-tile lists the grouped GEMMs walk.
+// per-expert compute batches -- here the row-tile list the grouped GEMMs walk.
 //
 // Three launches, all sized by the shape only (nothing is read back to the host):
 //   1. moe_plan_hist    one wavefront per chunk of kPlanChunk slots: expert histogram in LDS.
 //   2. moe_plan_scan    one workgroup: per-expert scan over chunks (chunk bases), counts, the
-//                     exclusive scan of counts (offsets), row-tile lists for 64/128/256-row
-//                     tiles, the expert order by decreasing count, the out-of-range total.
+//                     exclusive scan of counts (offsets), the row-tile list of 256-row tiles
+//                     with each expert's first index in it, the expert order by decreasing
+//                     count, the out-of-range total.
 //   3. moe_plan_scatter one wavefront per chunk, slots in ascending order, 64 at a time: lanes that
 //                     share an expert id find each other with one ballot per id bit, take
 //                     consecutive rows after the expert's running base in lane order, and the
@@ -81,11 +82,10 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wsum) {
 
 // The part of the scan kernel after the per-expert counts (every thread of the 1024 calls it;
 // thread e < E holds cnt = counts[e], every thread a partial count badp of out-of-range ids): counts, offsets (also left in s_off[0..E]), the three
-// row-tile lists, the longest-first expert order, src = -1 past the last routed row, the status.
+// row-tile list, the longest-first expert order, src = -1 past the last routed row, the status.
 __device__ void plan_finish(int N, int E, int cnt, int badp, int32_t* s_cnt, int32_t* s_off,
                             int32_t* wsum, int32_t* status, int32_t* counts, int32_t* offsets,
-                            int32_t* lpt, int32_t* src, int32_t* mt64, int32_t* mt128,
-                            int32_t* mt256) {
+                            int32_t* lpt, int32_t* src, int32_t* tstart, int32_t* mtiles) {
   const int tid = threadIdx.x;
   if (tid < E) counts[tid] = cnt;
   s_cnt[tid] = cnt;
@@ -97,18 +97,18 @@ __device__ void plan_finish(int N, int E, int cnt, int badp, int32_t* s_cnt, int
   if (tid < E) offsets[tid] = s_off[tid];
   if (tid == 0) offsets[E] = nvalid;
 
-  // row-tile lists: (expert, first row) of every tile of tile_rows rows, experts ascending
-  int32_t* lists[kNumTileSizes] = {mt64, mt128, mt256};
-  for (int t = 0; t < kNumTileSizes; ++t) {
-    const int bm = kTileRows[t];
-    const int nt = tid < E ? (cnt + bm - 1) / bm : 0;
+  // row-tile list: (expert, first row) of every row tile of kRowTile rows (the last of an expert
+  // holds the rest), experts ascending, and each expert's first index in the list
+  {
+    const int nt = tid < E ? (cnt + kRowTile - 1) / kRowTile : 0;
     const int ti = block_scan_1024(nt, wsum);
     if (tid < E) {
-      int2* list = (int2*)lists[t];
+      int2* list = (int2*)mtiles;
       const int start = ti - nt;
-      for (int q = 0; q < nt; ++q) list[start + q] = make_int2(tid, s_off[tid] + q * bm);
+      tstart[tid] = start;
+      for (int q = 0; q < nt; ++q) list[start + q] = make_int2(tid, s_off[tid] + q * kRowTile);
     }
-    if (tid == 1023) status[1 + t] = ti;
+    if (tid == 1023) status[1] = ti;
   }
 
   // experts by decreasing count (ties: lower index first)
@@ -127,14 +127,14 @@ __device__ void plan_finish(int N, int E, int cnt, int badp, int32_t* s_cnt, int
   const int bad = block_scan_1024(badp, wsum);
   if (tid == 1023) status[0] = bad;
   if (tid == 0)
-    for (int w = 1 + kNumTileSizes; w < kStatusWords; ++w) status[w] = 0;
+    for (int w = 2; w < kStatusWords; ++w) status[w] = 0;
 }
 
 __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int32_t* status,
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* blkhist, const int32_t* blkbad,
-                                                    int32_t* lpt, int32_t* src, int32_t* mt64,
-                                                    int32_t* mt128, int32_t* mt256) {
+                                                    int32_t* lpt, int32_t* src, int32_t* tstart,
+                                                    int32_t* mtiles) {
   __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t wsum[16];
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(1024) void moe_plan_scan(int N, int E, int NB, int3
   // out-of-range total: per-thread partial sums over the chunks
   int badp = 0;
   for (int b = tid; b < NB; b += 1024) badp += blkbad[b];
-  plan_finish(N, E, cnt, badp, s_cnt, s_off, wsum, status, counts, offsets, lpt, src, mt64,
-              mt128, mt256);
+  plan_finish(N, E, cnt, badp, s_cnt, s_off, wsum, status, counts, offsets, lpt, src, tstart,
+              mtiles);
 }
 
 // Orders a wavefront's LDS accesses before and after it, across its lanes (every lane's base
@@ -247,7 +247,7 @@ hipError_t launch_plan_scan(const moe_shape& s, const PlanLayout& L, const PlanP
                             hipStream_t st) {
   hipLaunchKernelGGL(moe_plan_scan, dim3(1), dim3(1024), 0, st, (int)L.N, (int)s.E, (int)L.NB,
                      p.status, p.counts, p.offsets, p.blkhist, p.blkbad, p.lpt, p.src,
-                     p.mtiles[0], p.mtiles[1], p.mtiles[2]);
+                     p.tstart, p.mtiles);
   return hipGetLastError();
 }
 
