@@ -95,7 +95,7 @@ def stage_work(w):
     }
 
 
-def cpu_baseline(inp, n_tokens):
+def cpu_baseline(inp, n_tokens, wgrad_expert=True):
     import oracle
     import workloads as W
 
@@ -105,7 +105,7 @@ def cpu_baseline(inp, n_tokens):
     oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks, inp.dout, mode="bf16")
     dt = time.perf_counter() - t0
     flops = 12 * w.K * w.D * w.F * len(toks)  # forward 6KDF + token-local backward 6KDF per token
-    return {
+    res = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
@@ -114,6 +114,19 @@ def cpu_baseline(inp, n_tokens):
                   "(out, dscores, dx; weight gradients excluded), %.1f s, %.3g tokens/s"
                   % (len(toks), w.name, dt, len(toks) / dt),
     }
+    if wgrad_expert and inp.dout is not None:
+        # the weight gradients of the most loaded expert, whole (the oracle's matmul form: the
+        # rows' gate/up products 4DF, da 2DF, dW2 2DF and dW13 4DF per row of the expert)
+        import numpy as np
+        ids = np.asarray(inp.ids).reshape(-1)
+        counts = np.bincount(ids[(ids >= 0) & (ids < w.E)], minlength=w.E)
+        e = int(np.argmax(counts))
+        t0 = time.perf_counter()
+        oracle.expert_wgrad(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e)
+        dw = time.perf_counter() - t0
+        res["wgrad_sample"] = {"expert": e, "rows": int(counts[e]), "s": round(dw, 2),
+                               "tflops": 12 * int(counts[e]) * w.D * w.F / dw / 1e12}
+    return res
 
 
 # ------------------------------------------------------------------------------------------------
@@ -568,11 +581,14 @@ def main():
     names = PLAN_STAGES + FWD_STAGES + bwd_stages
     per = {n: [] for n in names}
     step_ms = []
+    call_ms = {"plan": [], "forward": [], "backward": []}  # each whole ABI call
     for (tp, ep), (tf, ef), (tb, eb) in traces:
         for lst, evs in ((PLAN_STAGES, ep), (FWD_STAGES, ef), (bwd_stages, eb)):
             for i, n in enumerate(lst):
                 per[n].append(hip.ms(evs[i], evs[i + 1]))
         step_ms.append(hip.ms(ep[0], eb[-1]))
+        for c, evs in (("plan", ep), ("forward", ef), ("backward", eb)):
+            call_ms[c].append(hip.ms(evs[0], evs[-1]))
     work = stage_work(w)
     stages = {}
     for n in names:
@@ -624,6 +640,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "step_ms": spread(step_ms),
+        "call_ms": {c: spread(v) for c, v in call_ms.items()},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
