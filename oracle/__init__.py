@@ -77,7 +77,8 @@ def lib():
             L.oracle_swiglu_grad_array.restype = None
             L.oracle_swiglu_grad_array.argtypes = [S, I64, P, P, P, P, P]
             L.oracle_wgrad_entries.restype = ctypes.c_int
-            L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P, P, P]
+            L.oracle_wgrad_entries.argtypes = [S, P, P, P, P, P, P, I64, I64, P, P, I64, P, P, P, P,
+                                               P, P]
             L.oracle_route.restype = ctypes.c_int
             L.oracle_route.argtypes = [I64, I64, I64, P, ctypes.c_int32, ctypes.c_int32, I64, I64,
                                        P, P]
@@ -213,10 +214,12 @@ def tokens(x, ids, scores, w13, w2, toks, dout=None, mode: str = "bf16", want_y:
 
 
 def wgrad_entries(x, ids, scores, w13, w2, dout, e: int, jd: np.ndarray, df: np.ndarray,
-                  mode: str = "bf16", wgrad_f32: bool = False, init13=None, init2=None):
+                  mode: str = "bf16", wgrad_f32: bool = False, init13=None, init2=None,
+                  scales: bool = False):
     """dW13[e, j, d] for the (j, d) pairs in jd ([n,2], j in [0,2F)) and dW2[e, d, f] for the
     (d, f) pairs in df ([m,2]); init13 / init2: existing values of those entries to accumulate
-    into."""
+    into. Returns (v13, v2), or with scales (v13, v2, rss13, rss2): also each entry's
+    root-sum-square of terms."""
     T, D = x.shape
     E, _, F, _ = w13.shape
     K = ids.shape[1]
@@ -230,10 +233,11 @@ def wgrad_entries(x, ids, scores, w13, w2, dout, e: int, jd: np.ndarray, df: np.
     ids64 = np.ascontiguousarray(ids, dtype=np.int64)
     sc = np.ascontiguousarray(scores, dtype=np.float64)
     v13 = np.zeros(len(jd)); v2 = np.zeros(len(df))
+    r13, r2 = (np.zeros(len(jd)), np.zeros(len(df))) if scales else (None, None)
     lib().oracle_wgrad_entries(ctypes.byref(sh), _p(x), _p(ids64), _p(sc), _p(w13), _p(w2),
                                _p(dout), int(e), len(jd), _p(jd), _p(v13), len(df), _p(df), _p(v2),
-                               _p(i13), _p(i2))
-    return v13, v2
+                               _p(i13), _p(i2), _p(r13), _p(r2))
+    return (v13, v2, r13, r2) if scales else (v13, v2)
 
 
 def _widen(a, in_dtype):

@@ -456,12 +456,13 @@ int oracle_tokens(const oracle_shape* s, const void* x, const int64_t* ids, cons
  *   dw2_vals[p]  = dW2[e, df[2p], df[2p+1]]   (d in [0,D), f in [0,F)).
  * The sums run over the expert's rows in ascending row order, i.e. the slots i with ids_i = e in
  * ascending i (the stable grouped order). Each needed column f of the intermediate is evaluated per
- * row from its definition. */
+ * row from its definition. dw13_rss / dw2_rss (optional): the root-sum-square of each entry's
+ * terms, as for the whole-layer evaluation. */
 int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* ids,
                          const double* scores, const void* w13, const void* w2, const void* dout,
                          int64_t e, int64_t n13, const int64_t* jd, double* dw13_vals, int64_t n2,
                          const int64_t* df, double* dw2_vals, const double* dw13_init,
-                         const double* dw2_init) {
+                         const double* dw2_init, double* dw13_rss, double* dw2_rss) {
   const int64_t D = s->D, F = s->F, K = s->K, N = s->T * s->K;
   /* distinct intermediate columns f that the requested entries need */
   int64_t* fl = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n13 + n2 + 1));
@@ -479,6 +480,8 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
     for (int64_t p = 0; p < n13; ++p) need13 |= (jd[2 * p] % F == f);
     double* acc13 = (double*)calloc((size_t)(n13 + 1), sizeof(double));
     double* acc2 = (double*)calloc((size_t)(n2 + 1), sizeof(double));
+    double* sq13 = (double*)calloc((size_t)(n13 + 1), sizeof(double));
+    double* sq2 = (double*)calloc((size_t)(n2 + 1), sizeof(double));
     double* xrow = (double*)malloc(sizeof(double) * D);
     double* dyrow = (double*)malloc(sizeof(double) * D);
     for (int64_t i = 0; i < N; ++i) {
@@ -491,7 +494,11 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
       for (int64_t d = 0; d < D; ++d)
         dyrow[d] = R(s, scores[i] * ld(dout, t * D + d, s->in_dtype));
       for (int64_t p = 0; p < n2; ++p)
-        if (df[2 * p + 1] == f) acc2[p] += dyrow[df[2 * p]] * av;
+        if (df[2 * p + 1] == f) {
+          const double term = dyrow[df[2 * p]] * av;
+          acc2[p] += term;
+          sq2[p] += term * term;
+        }
       if (need13) {
         const double da = da_elem(s, w2, e, f, dyrow);
         double dg, du;
@@ -499,15 +506,23 @@ int oracle_wgrad_entries(const oracle_shape* s, const void* x, const int64_t* id
         for (int64_t p = 0; p < n13; ++p) {
           const int64_t j = jd[2 * p];
           if (j % F != f) continue;
-          acc13[p] += (j < F ? dg : du) * xrow[jd[2 * p + 1]];
+          const double term = (j < F ? dg : du) * xrow[jd[2 * p + 1]];
+          acc13[p] += term;
+          sq13[p] += term * term;
         }
       }
     }
     for (int64_t p = 0; p < n2; ++p)
-      if (df[2 * p + 1] == f) dw2_vals[p] = RW(s, (dw2_init ? dw2_init[p] : 0.0) + acc2[p]);
+      if (df[2 * p + 1] == f) {
+        dw2_vals[p] = RW(s, (dw2_init ? dw2_init[p] : 0.0) + acc2[p]);
+        if (dw2_rss) dw2_rss[p] = sqrt(sq2[p]);
+      }
     for (int64_t p = 0; p < n13; ++p)
-      if (jd[2 * p] % F == f) dw13_vals[p] = RW(s, (dw13_init ? dw13_init[p] : 0.0) + acc13[p]);
-    free(acc13); free(acc2); free(xrow); free(dyrow);
+      if (jd[2 * p] % F == f) {
+        dw13_vals[p] = RW(s, (dw13_init ? dw13_init[p] : 0.0) + acc13[p]);
+        if (dw13_rss) dw13_rss[p] = sqrt(sq13[p]);
+      }
+    free(acc13); free(acc2); free(sq13); free(sq2); free(xrow); free(dyrow);
   }
   free(fl);
   return 0;

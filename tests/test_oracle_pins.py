@@ -369,7 +369,7 @@ def test_empty_expert_weight_grads_are_zero():
 def test_sampled_functions_agree_with_full():
     w = W.PARITY_WORKLOADS["p_skew"].with_(T=60)
     inp = W.make_inputs(w)
-    full = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout)
+    full = oracle.full(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, scales=True)
     toks = np.array([0, 7, 59])
     tk = oracle.tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks, inp.dout, want_y=True)
     np.testing.assert_array_equal(tk["out"], full["out"][toks])
@@ -379,10 +379,15 @@ def test_sampled_functions_agree_with_full():
     jd = W.sample_pairs(2 * w.F, w.D, 40, 1, 1)
     df = W.sample_pairs(w.D, w.F, 40, 1, 2)
     for e in (0, 3):
-        v13, v2 = oracle.wgrad_entries(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dout, e,
-                                       jd, df)
+        v13, v2, r13, r2 = oracle.wgrad_entries(inp.x, inp.ids, inp.scores, inp.w13, inp.w2,
+                                                inp.dout, e, jd, df, scales=True)
         np.testing.assert_array_equal(v13, full["dw13"][e].reshape(2 * w.F, w.D)[jd[:, 0], jd[:, 1]])
         np.testing.assert_array_equal(v2, full["dw2"][e][df[:, 0], df[:, 1]])
+        # the per-entry root-sum-square of terms: the same terms in the same order as the
+        # whole-layer evaluation
+        np.testing.assert_allclose(
+            r13, full["dw13_rss"][e].reshape(2 * w.F, w.D)[jd[:, 0], jd[:, 1]], rtol=1e-13, atol=0)
+        np.testing.assert_allclose(r2, full["dw2_rss"][e][df[:, 0], df[:, 1]], rtol=1e-13, atol=0)
 
 
 # ------------------------------------------------------------------------------------------------
