@@ -11,9 +11,17 @@ ABI's header), in the launch configuration of the timed path.
   itself with 32-bit offsets up to the end of x; and x of exactly 4 GiB, where the forward keeps
   the gathered rows instead. Checked: out, dscores, dx on sampled tokens including the last,
   and dW entries of three experts.
+* The plan at the largest slot count accepted (T*K = 2^31 - 2^16 slots: T = 2^25 - 1024, K = 64,
+  1024 experts, int32 ids): counts, offsets, pos and src bit-exact. At this size the stable
+  grouping is checked through the properties that determine it uniquely (a full stable argsort
+  of 2^31 ids would take the oracle minutes): counts = the histogram of the ids, offsets = their
+  exclusive prefix sum, every grouped row r of segment e holds a slot src[r] routed to e, src
+  increases within each segment (stability), and pos[src[r]] = r for every r (src is the
+  inverse permutation of pos).
 
-The bar is the elementwise one of every GPU parity test (parity_check). Inputs are the seeded
-draws of the workloads module at these shapes.
+The bar for floating outputs is the elementwise one of every GPU parity test (parity_check).
+Inputs are the seeded draws of the workloads module at these shapes; the slot-limit ids are
+seeded uniform draws.
 """
 import gc
 import time
@@ -128,3 +136,67 @@ def test_token_rows_at_4_gib(T):
     jd = _corners_and_seeded(2 * F, D, 4, 12, 1)
     df = _corners_and_seeded(D, F, 4, 12, 2)
     _run_and_check(w, toks, [0, 3, E - 1], jd, df)
+
+
+def _uniform_ids(n, E, seed, block=1 << 26):
+    """Seeded uniform int32 expert ids, drawn in independent blocks on a few threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(n, dtype=np.int32)
+    nblk = (n + block - 1) // block
+    seqs = np.random.SeedSequence([seed, 31]).spawn(nblk)
+
+    def fill(b):
+        lo, hi = b * block, min(n, (b + 1) * block)
+        g = np.random.Generator(np.random.PCG64(seqs[b]))
+        out[lo:hi] = g.integers(0, E, hi - lo, dtype=np.int32)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(fill, range(nblk)))
+    return out
+
+
+def test_plan_at_the_slot_limit():
+    import mixture_experts_routed_plan_amd as M
+    T, K, E = 2**25 - 1024, 64, 1024
+    N = T * K
+    assert N == 2**31 - 2**16
+    s = M.make_shape(T, 64, 64, E, K, M.MOE_IDS_I32, False)
+    nb = M.moe_plan_bytes(s)
+    assert nb > 0
+    t0 = time.time()
+    ids = _uniform_ids(N, E, 13)
+    log("\n[slot limit] %d ids drawn in %.1fs" % (N, time.time() - t0))
+    d_ids = torch.from_numpy(ids).cuda()
+    plan = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    M.check(M.moe_plan(s, d_ids, plan), "moe_plan")
+    st, bad = M.moe_plan_status(s, plan)
+    M.check(st, "moe_plan_status")
+    assert bad == 0
+    del d_ids
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty(N, dtype=torch.int32, device="cuda")
+    src = torch.empty(N, dtype=torch.int32, device="cuda")
+    M.check(M.moe_plan_export(s, plan, counts, offsets, pos, src), "moe_plan_export")
+    torch.cuda.synchronize()
+    del plan
+    counts, offsets = counts.cpu().numpy(), offsets.cpu().numpy()
+    pos_h = pos.cpu().numpy()
+    del pos
+    src_h = src.cpu().numpy()
+    del src
+    torch.cuda.empty_cache()
+    log("[slot limit] gpu plan done, arrays on the host after %.1fs" % (time.time() - t0))
+
+    ref_counts = np.bincount(ids, minlength=E)
+    np.testing.assert_array_equal(counts, ref_counts)
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(ref_counts)]))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        seg = src_h[lo:hi]
+        assert (ids[seg] == e).all(), "segment %d holds a slot of another expert" % e
+        assert (np.diff(seg) > 0).all(), "segment %d is not in ascending slot order" % e
+        assert (pos_h[seg] == np.arange(lo, hi, dtype=np.int32)).all(), "pos/src of segment %d" % e
+    log("[slot limit] plan checked in %.1fs" % (time.time() - t0))
+    del ids, pos_h, src_h
+    gc.collect()
