@@ -5,6 +5,11 @@ pointers are used), raw integer addresses or None.
 
 The library must be built (``python mixture_experts_routed_plan_amd/build.py``); importing this
 package without it raises ImportError -- there is no fallback implementation.
+
+With MOE_ROUTED_LIBRARY=checked in the environment the package loads libmoe_routed_checked.so
+instead (include/moe_routed_checked.h: the same entry points, with every global memory access of
+the kernels tested against its buffer) and binds moe_checked_violations, moe_checked_reset and
+moe_checked_shrink as well. The choice is made once, at import.
 """
 from __future__ import annotations
 
@@ -12,7 +17,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_routed.so")
+CHECKED = os.environ.get("MOE_ROUTED_LIBRARY", "") == "checked"
+LIB_PATH = os.path.join(_HERE, "libmoe_routed_checked.so" if CHECKED else "libmoe_routed.so")
 
 MOE_IDS_I32 = 0
 MOE_IDS_I64 = 1
@@ -119,6 +125,12 @@ def _load():
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_abi_version": (ctypes.c_int, []),
     }
+    if CHECKED:
+        sigs.update({
+            "moe_checked_violations": (St, [ctypes.POINTER(ctypes.c_uint64)]),
+            "moe_checked_reset": (St, []),
+            "moe_checked_shrink": (St, [ctypes.c_int64]),
+        })
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
         fn.restype = res
@@ -254,6 +266,21 @@ def moe_saved_views(shape, saved):
     if st != MOE_OK:
         raise MoeError(st, "moe_saved_views")
     return tuple(p.value for p in ptrs)
+
+
+def moe_checked_violations() -> int:
+    """Checked library only: accesses found outside their buffer since load or the last reset."""
+    n = ctypes.c_uint64(0)
+    check(_lib.moe_checked_violations(ctypes.byref(n)), "moe_checked_violations")
+    return n.value
+
+
+def moe_checked_reset() -> None:
+    check(_lib.moe_checked_reset(), "moe_checked_reset")
+
+
+def moe_checked_shrink(nbytes: int) -> None:
+    check(_lib.moe_checked_shrink(int(nbytes)), "moe_checked_shrink")
 
 
 def check(status: int, what: str = "") -> None:

@@ -5,8 +5,15 @@
 #include <mutex>
 
 #include "moe_internal.h"
+#ifdef MOE_CHECKED
+#include "moe_routed_checked.h"
+#endif
 
 using namespace moe;
+
+#ifdef MOE_CHECKED
+int64_t moe::g_checked_shrink = 0;
+#endif
 
 namespace {
 
@@ -395,5 +402,44 @@ moe_status moe_saved_views(const moe_shape* s, void* saved, uint16_t** xg, uint1
   if (y) *y = (uint16_t*)(b + S.y);
   return MOE_OK;
 }
+
+#ifdef MOE_CHECKED
+// Checked build only (declared in moe_routed_checked.h).
+moe_status moe_checked_violations(uint64_t* count) {
+  if (!count) return MOE_E_NULL;
+  hipError_t (*const counters[])(unsigned int**) = {oob_counter_plan, oob_counter_rowops,
+                                                    oob_counter_gemm};
+  MOE_TRY(hipDeviceSynchronize());
+  uint64_t total = 0;
+  for (auto f : counters) {
+    unsigned int* d = nullptr;
+    unsigned int h = 0;
+    MOE_TRY(f(&d));
+    MOE_TRY(hipMemcpy(&h, d, sizeof h, hipMemcpyDeviceToHost));
+    total += h;
+  }
+  *count = total;
+  return MOE_OK;
+}
+
+moe_status moe_checked_reset(void) {
+  hipError_t (*const counters[])(unsigned int**) = {oob_counter_plan, oob_counter_rowops,
+                                                    oob_counter_gemm};
+  MOE_TRY(hipDeviceSynchronize());
+  for (auto f : counters) {
+    unsigned int* d = nullptr;
+    const unsigned int zero = 0;
+    MOE_TRY(f(&d));
+    MOE_TRY(hipMemcpy(d, &zero, sizeof zero, hipMemcpyHostToDevice));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_checked_shrink(int64_t bytes) {
+  if (bytes < 0) return MOE_E_SHAPE;
+  g_checked_shrink = bytes;
+  return MOE_OK;
+}
+#endif
 
 }  // extern "C"

@@ -95,6 +95,9 @@ struct GemmArgs {
   // P rows gathered from token rows (fused permute): P row r is row src[r] / gather_k of P
   const int32_t* gather_src;   // null: P rows are the routed rows themselves
   int gather_k;
+  // extents in bytes of P, Q, C (or Cf), C2, H and gather_src from those pointers; the checked
+  // build tests every access against them
+  uint64_t ext_p, ext_q, ext_c, ext_c2, ext_h, ext_src;
 };
 
 // LDS tile layout: [rows][BK] bf16, each row BK/8 chunks of 16 bytes; logical chunk c of row r
@@ -207,6 +210,10 @@ struct DmaTile {
   static constexpr int NB = R / 8 / kWaves;  // blocks per wavefront = copy actions per stage
   const char* base;                  // uniform
   uint32_t off[NB];                  // per lane, bytes from base (k = 0)
+#ifdef MOE_CHECKED
+  const char* lo;                    // the operand's buffer and its extent in bytes
+  uint64_t ext;
+#endif
 
   // row_off(row) -> byte offset of the start of tile row `row` (0 <= row < R) from base
   template <typename RowOff>
@@ -223,6 +230,9 @@ struct DmaTile {
   // lds_tile: LDS byte address of the tile
   __device__ __forceinline__ void issue(uint32_t lds_tile, int k0, int i) const {
     const int blk = (threadIdx.x >> 6) * NB + i;
+#ifdef MOE_CHECKED
+    if (__any(!moe_check_range(base + (int64_t)k0 * 2 + off[i], 16, lo, ext))) return;
+#endif
     dma16(base + (int64_t)k0 * 2, off[i], lds_tile + blk * 8 * kBK * 2);
   }
 };
@@ -243,6 +253,10 @@ struct MnTile {
   int64_t ldb;        // bytes between k rows
   uint32_t col[NB];   // per lane: byte offset of its 16-byte chunk within a row (clamped)
   int row[NB];        // per lane: k row within a stage (0..63)
+#ifdef MOE_CHECKED
+  const char* lo;     // the operand's buffer and its extent in bytes
+  uint64_t ext;
+#endif
 
   __device__ __forceinline__ void init(const void* b, int64_t ld, int idx0, int idx_lim) {
     base = uniform_ptr(b);
@@ -265,6 +279,11 @@ struct MnTile {
     const int blk = (threadIdx.x >> 6) * NB + i;
     int k = k0 + row[i];
     if (k > klim - 1) k = klim - 1;  // k0 <= klim - 1 whenever the stage exists
+#ifdef MOE_CHECKED
+    if (__any(!moe_check_range(base + (int64_t)k0 * ldb + (uint32_t)((k - k0) * ldb) + col[i], 16,
+                               lo, ext)))
+      return;
+#endif
     dma16(base + (int64_t)k0 * ldb, (uint32_t)((k - k0) * ldb) + col[i], lds_tile + blk * 2 * R * 2);
   }
 };
@@ -328,6 +347,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
       pd.init(g.P, [&](int row) -> uint32_t {
         int r = r0 + row;
         if (r > rl - 1) r = rl - 1;
+        if (!MOE_IN(src + r, 4, src, g.ext_src)) return 0u;
         return (uint32_t)((int64_t)(src[r] / kk) * ldb);
       });
     } else {
@@ -367,6 +387,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
     qm.init(qbase + (int64_t)t.kbeg * g.ldq + t.n0, g.ldq, 0, g.N_out - t.n0);
   }
 
+#ifdef MOE_CHECKED
+  pd.lo = pm.lo = (const char*)g.P;
+  pd.ext = pm.ext = g.ext_p;
+  qd.lo = qm.lo = (const char*)g.Q;
+  qd.ext = qm.ext = g.ext_q;
+#endif
   f32x16 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -552,17 +578,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
   };
   // read row segments of width W (bf16) out of a [32][W + 4] area and store them
   auto flush = [&](const uint16_t* area, int W, uint16_t* dst, int64_t ld, int row0, int rlim,
-                   int col0, int clim) {
+                   int col0, int clim, const void* lo, uint64_t ext) {
     const int per_row = W / 8;            // 16-byte chunks per row
     const int rows_per_pass = 64 / per_row;
 #pragma unroll
     for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
       const int row = pass * rows_per_pass + lane / per_row, ch = lane % per_row;
       const uint16_t* src = area + row * (W + 4) + ch * 8;
-      const uint2 lo = *(const uint2*)src, hi = *(const uint2*)(src + 4);
+      const uint2 lo4 = *(const uint2*)src, hi4 = *(const uint2*)(src + 4);
       const int r = row0 + row, c = col0 + ch * 8;
-      if (r < rlim && c < clim)
-        *(uint4*)(dst + (int64_t)r * ld + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      if (r < rlim && c < clim && MOE_IN(dst + (int64_t)r * ld + c, 16, lo, ext))
+        *(uint4*)(dst + (int64_t)r * ld + c) = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
     }
   };
   if constexpr (EPI == EPI_STORE && OUT != OUT_BF16) {
@@ -592,10 +618,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
           const bool in = r < t.r_lim && c < g.N_out;
           const int64_t o = cofs + (int64_t)(in ? r : 0) * g.ldc + (in ? c : 0);
           if constexpr (OUT == OUT_BF16_ACC) {
-            oldb[pass] = *(const uint4*)(g.C + o);
+            oldb[pass] = MOE_IN(g.C + o, 16, g.C, g.ext_c) ? *(const uint4*)(g.C + o)
+                                                            : make_uint4(0, 0, 0, 0);
           } else {
-            oldf[2 * pass] = *(const float4*)(g.Cf + o);
-            oldf[2 * pass + 1] = *(const float4*)(g.Cf + o + 4);
+            const bool ok = MOE_IN(g.Cf + o, 32, g.Cf, g.ext_c);
+            oldf[2 * pass] = ok ? *(const float4*)(g.Cf + o) : make_float4(0, 0, 0, 0);
+            oldf[2 * pass + 1] = ok ? *(const float4*)(g.Cf + o + 4) : make_float4(0, 0, 0, 0);
           }
         }
       }
@@ -616,8 +644,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
         *(float4*)&v[0] = *(const float4*)src;
         *(float4*)&v[4] = *(const float4*)(src + 4);
         const int r = row0 + row, c = col0 + ch * 8;
-        if (r < t.r_lim && c < g.N_out) {
-          const int64_t o = cofs + (int64_t)r * g.ldc + c;
+        const int64_t o = cofs + (int64_t)r * g.ldc + c;
+        if (r < t.r_lim && c < g.N_out &&
+            MOE_IN(OUT == OUT_BF16_ACC ? (const void*)(g.C + o) : (const void*)(g.Cf + o),
+                   OUT == OUT_BF16_ACC ? 16 : 32, g.Cf, g.ext_c)) {
           if constexpr (OUT == OUT_BF16_ACC) {
             const uint4 old = oldb[pass];
             const uint32_t w[4] = {old.x, old.y, old.z, old.w};
@@ -655,7 +685,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
           *(uint2*)(ep + rl * PW + i * 32 + gq * 8 + cq) =
               make_uint2(pk2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]),
                          pk2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]));
-      flush(ep, WN, C, g.ldc, t.r0 + (wr + WR * j) * 32, t.r_lim, t.n0 + wc * WN, g.N_out);
+      flush(ep, WN, C, g.ldc, t.r0 + (wr + WR * j) * 32, t.r_lim, t.n0 + wc * WN, g.N_out, g.C,
+            g.ext_c);
     }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
     // the wavefront's 64 activation columns f0w .. f0w+63: a, g and u each through [32][68]
@@ -684,10 +715,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
           *(uint2*)(ea + o) = make_uint2(pk2(av[0], av[1]), pk2(av[2], av[3]));
         }
       const int row0 = t.r0 + (wr + WR * j) * 32;
-      flush(ea, W, g.C2, g.ldc2, row0, t.r_lim, f0w, g.F);
+      flush(ea, W, g.C2, g.ldc2, row0, t.r_lim, f0w, g.F, g.C2, g.ext_c2);
       if (g.C) {
-        flush(eg, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
-        flush(eu, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
+        flush(eg, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F, g.C, g.ext_c);
+        flush(eu, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F, g.C, g.ext_c);
       }
     }
   } else {  // EPI_SWIGLU_BWD: acc = da over columns f; g, u come from the saved h13
@@ -714,7 +745,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
           int c = f0w + ch * 8;
           if (c > g.F - 8) c = g.F - 8;
           const uint16_t* hrow = g.H + (int64_t)r * g.ldh + c;
-          const uint4 gv = *(const uint4*)hrow, uv = *(const uint4*)(hrow + g.F);
+          const bool hok = MOE_IN(hrow, 16, g.H, g.ext_h) && MOE_IN(hrow + g.F, 16, g.H, g.ext_h);
+          const uint4 gv = hok ? *(const uint4*)hrow : make_uint4(0, 0, 0, 0);
+          const uint4 uv = hok ? *(const uint4*)(hrow + g.F) : make_uint4(0, 0, 0, 0);
           uint16_t* d1 = e1 + row * PW + ch * 8;
           uint16_t* d2 = e2 + row * PW + ch * 8;
           *(uint2*)d1 = make_uint2(gv.x, gv.y);
@@ -743,8 +776,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint16_t* lds, int 
             *(uint2*)(e1 + o) = make_uint2(pk2(dg[0], dg[1]), pk2(dg[2], dg[3]));
             *(uint2*)(e2 + o) = make_uint2(pk2(du[0], du[1]), pk2(du[2], du[3]));
           }
-        flush(e1, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F);
-        flush(e2, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F);
+        flush(e1, W, g.C, g.ldc, row0, t.r_lim, f0w, g.F, g.C, g.ext_c);
+        flush(e2, W, g.C + g.F, g.ldc, row0, t.r_lim, f0w, g.F, g.C, g.ext_c);
       }
     }
   }
@@ -808,6 +841,15 @@ hipError_t launch(void (*kernel)(GemmArgs), const GemmArgs& g, int grid, hipStre
   return hipGetLastError();
 }
 
+// an extent in bytes as the kernels see it (checked builds: shortened by g_checked_shrink)
+uint64_t ext(int64_t bytes) {
+#ifdef MOE_CHECKED
+  return bytes > g_checked_shrink ? (uint64_t)(bytes - g_checked_shrink) : 0;
+#else
+  return (uint64_t)bytes;
+#endif
+}
+
 GemmArgs rows_args(const moe_shape& s, const PlanPtrs& p) {
   GemmArgs g{};
   g.F = (int)s.F;
@@ -843,14 +885,17 @@ hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
                             const uint16_t* w13, uint16_t* h13, uint16_t* a, hipStream_t st,
                             bool gather) {
   GemmArgs g = rows_args(s, p);
-  g.P = xg; g.ldp = s.D;
+  const int64_t N = s.T * s.K;
+  g.P = xg; g.ldp = s.D; g.ext_p = ext(2 * N * s.D);
   if (gather) {  // xg is x: P rows come from the routed rows' tokens
     g.gather_src = p.src;
     g.gather_k = (int)s.K;
+    g.ext_p = ext(2 * s.T * s.D);
+    g.ext_src = ext(4 * N);
   }
-  g.Q = w13; g.ldq = s.D; g.q_estride = 2 * s.F * s.D;
-  g.C = h13; g.ldc = 2 * s.F;
-  g.C2 = a; g.ldc2 = s.F;
+  g.Q = w13; g.ldq = s.D; g.q_estride = 2 * s.F * s.D; g.ext_q = ext(2 * s.E * 2 * s.F * s.D);
+  g.C = h13; g.ldc = 2 * s.F; g.ext_c = ext(2 * N * 2 * s.F);
+  g.C2 = a; g.ldc2 = s.F; g.ext_c2 = ext(2 * N * s.F);
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
   const int ntn = (int)ceil_div(s.F, kBN / 2);
   return launch(moe_fprop_w13_swiglu, g, rows_grid(s, ntn), st);
@@ -859,9 +904,10 @@ hipError_t launch_fprop_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
 hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t* a,
                            const uint16_t* w2, uint16_t* y, hipStream_t st) {
   GemmArgs g = rows_args(s, p);
-  g.P = a; g.ldp = s.F;
-  g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F;
-  g.C = y; g.ldc = s.D;
+  const int64_t N = s.T * s.K;
+  g.P = a; g.ldp = s.F; g.ext_p = ext(2 * N * s.F);
+  g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F; g.ext_q = ext(2 * s.E * s.D * s.F);
+  g.C = y; g.ldc = s.D; g.ext_c = ext(2 * N * s.D);
   g.N_out = (int)s.D; g.Kdim = (int)s.F;
   const int ntn = (int)ceil_div(s.D, kBN);
   return launch(moe_fprop_w2, g, rows_grid(s, ntn), st);
@@ -870,10 +916,12 @@ hipError_t launch_fprop_w2(const moe_shape& s, const PlanPtrs& p, const uint16_t
 static GemmArgs dgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint16_t* dy,
                               const uint16_t* w2, const uint16_t* h13, uint16_t* dh13) {
   GemmArgs g = rows_args(s, p);
-  g.P = dy; g.ldp = s.D;
+  const int64_t N = s.T * s.K;
+  g.P = dy; g.ldp = s.D; g.ext_p = ext(2 * N * s.D);
   g.Q = w2; g.ldq = s.F; g.q_estride = s.D * s.F;  // w2[e] read as [k = d][c = f]
-  g.C = dh13; g.ldc = 2 * s.F;
-  g.H = h13; g.ldh = 2 * s.F;
+  g.ext_q = ext(2 * s.E * s.D * s.F);
+  g.C = dh13; g.ldc = 2 * s.F; g.ext_c = ext(2 * N * 2 * s.F);
+  g.H = h13; g.ldh = 2 * s.F; g.ext_h = ext(2 * N * 2 * s.F);
   g.N_out = (int)s.F; g.Kdim = (int)s.D;
   return g;
 }
@@ -882,9 +930,11 @@ static GemmArgs wgrad_w2_args(const moe_shape& s, const PlanPtrs& p, const uint1
                               const uint16_t* a, void* dw2) {
   GemmArgs g{};
   g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
-  g.P = dy; g.ldp = s.D;  // [k = routed row][r = d]
-  g.Q = a; g.ldq = s.F;   // [k = routed row][c = f]
+  const int64_t N = s.T * s.K, wb = (s.flags & MOE_WGRAD_F32) ? 4 : 2;
+  g.P = dy; g.ldp = s.D; g.ext_p = ext(2 * N * s.D);  // [k = routed row][r = d]
+  g.Q = a; g.ldq = s.F; g.ext_q = ext(2 * N * s.F);   // [k = routed row][c = f]
   g.C = (uint16_t*)dw2; g.Cf = (float*)dw2; g.ldc = s.F; g.c_estride = s.D * s.F;
+  g.ext_c = ext(wb * s.E * s.D * s.F);
   g.M_out = (int)s.D; g.N_out = (int)s.F;
   return g;
 }
@@ -903,9 +953,11 @@ hipError_t launch_w2_backward(const moe_shape& s, const PlanPtrs& p, const uint1
 hipError_t launch_dgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_t* dh13,
                             const uint16_t* w13, uint16_t* dxg, hipStream_t st) {
   GemmArgs g = rows_args(s, p);
-  g.P = dh13; g.ldp = 2 * s.F;
+  const int64_t N = s.T * s.K;
+  g.P = dh13; g.ldp = 2 * s.F; g.ext_p = ext(2 * N * 2 * s.F);
   g.Q = w13; g.ldq = s.D; g.q_estride = 2 * s.F * s.D;  // w13[e] read as [k = j][c = d]
-  g.C = dxg; g.ldc = s.D;
+  g.ext_q = ext(2 * s.E * 2 * s.F * s.D);
+  g.C = dxg; g.ldc = s.D; g.ext_c = ext(2 * N * s.D);
   g.N_out = (int)s.D; g.Kdim = (int)(2 * s.F);
   const int ntn = (int)ceil_div(s.D, kBN);
   return launch(moe_dgrad_w13, g, rows_grid(s, ntn), st);
@@ -916,12 +968,18 @@ hipError_t launch_wgrad_w13(const moe_shape& s, const PlanPtrs& p, const uint16_
                             const uint16_t* xg, void* dw13, hipStream_t st) {
   GemmArgs g{};
   g.F = (int)s.F; g.E = (int)s.E; g.offsets = p.offsets; g.lpt = p.lpt;
-  g.P = dh13; g.ldp = 2 * s.F;  // [k = routed row][r = j]
-  g.Q = xg; g.ldq = s.D;        // [k = routed row][c = d]
+  const int64_t N = s.T * s.K, wb = (s.flags & MOE_WGRAD_F32) ? 4 : 2;
+  g.P = dh13; g.ldp = 2 * s.F; g.ext_p = ext(2 * N * 2 * s.F);  // [k = routed row][r = j]
+  g.Q = xg; g.ldq = s.D; g.ext_q = ext(2 * N * s.D);            // [k = routed row][c = d]
   g.C = (uint16_t*)dw13; g.Cf = (float*)dw13; g.ldc = s.D; g.c_estride = 2 * s.F * s.D;
+  g.ext_c = ext(wb * s.E * 2 * s.F * s.D);
   g.M_out = (int)(2 * s.F); g.N_out = (int)s.D;
   const int grid = (int)(s.E * ceil_div(2 * s.F, kBM) * ceil_div(s.D, kBN));
   return launch(wgrad_w13_kernel(s), g, grid, st);
 }
+
+#ifdef MOE_CHECKED
+hipError_t oob_counter_gemm(unsigned int** p) { return oob_counter_address(p); }
+#endif
 
 }  // namespace moe

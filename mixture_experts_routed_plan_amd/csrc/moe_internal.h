@@ -136,6 +136,41 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 }
 
 // ------------------------------------------------------------------------------------------
+// checked builds (compiled with MOE_CHECKED into libmoe_routed_checked.so): the kernels test
+// their global memory accesses against the extent of the buffer each belongs to. An access
+// outside is not made (a copy or store is skipped, a load reads zeros) and is counted in a device
+// word of the kernel's source file, which moe_checked_violations sums on the host. In the
+// product build the tests compile to nothing.
+#ifdef MOE_CHECKED
+static __device__ unsigned int g_oob_count;
+__device__ __forceinline__ bool moe_check(bool ok) {
+  if (!ok) atomicAdd(&g_oob_count, 1u);
+  return ok;
+}
+// [p, p + n) lies within [lo, lo + bytes)
+__device__ __forceinline__ bool moe_check_range(const void* p, uint64_t n, const void* lo,
+                                                uint64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p, b = (uint64_t)(uintptr_t)lo;
+  return moe_check(lo != nullptr && a >= b && a - b <= bytes && n <= bytes - (a - b));
+}
+#define MOE_CHECK(cond) ::moe::moe_check(cond)
+#define MOE_IN(p, n, lo, bytes) ::moe::moe_check_range((p), (n), (lo), (bytes))
+// the device address of this source file's counter
+static inline hipError_t oob_counter_address(unsigned int** p) {
+  return hipGetSymbolAddress((void**)p, HIP_SYMBOL(g_oob_count));
+}
+hipError_t oob_counter_plan(unsigned int** p);
+hipError_t oob_counter_rowops(unsigned int** p);
+hipError_t oob_counter_gemm(unsigned int** p);
+// host side: every extent the GEMM launchers pass is shortened by this many bytes (a test of the
+// checks themselves: accesses near the end of a buffer then count although they are valid)
+extern int64_t g_checked_shrink;
+#else
+#define MOE_CHECK(cond) true
+#define MOE_IN(p, n, lo, bytes) true
+#endif
+
+// ------------------------------------------------------------------------------------------
 // launchers (return hipSuccess or the launch error)
 
 struct PlanPtrs {

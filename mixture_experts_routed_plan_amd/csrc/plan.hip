@@ -106,7 +106,9 @@ __device__ void plan_finish(int N, int E, int cnt, int badp, int32_t* s_cnt, int
       int2* list = (int2*)mtiles;
       const int start = ti - nt;
       tstart[tid] = start;
-      for (int q = 0; q < nt; ++q) list[start + q] = make_int2(tid, s_off[tid] + q * kRowTile);
+      for (int q = 0; q < nt; ++q)
+        if (MOE_CHECK(start + q < (N + kRowTile - 1) / kRowTile + E))
+          list[start + q] = make_int2(tid, s_off[tid] + q * kRowTile);
     }
     if (tid == 1023) status[1] = ti;
   }
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(64) void moe_plan_scatter(const IdT* __restrict__ i
     if (ok) p = base[v] + rank;
     lds_wave_sync();  // the workgroup is this one wavefront
     if (in) pos[i] = p;
-    if (ok) src[p] = i;
+    if (ok && MOE_CHECK(p >= 0 && p < N)) src[p] = i;
     if (ok && rank == 0) base[v] += cnt;
     lds_wave_sync();
   }
@@ -264,5 +266,9 @@ hipError_t launch_plan_scatter(const moe_shape& s, const PlanLayout& L, const Pl
                        N, E, NB, nbits, p.offsets, p.blkhist, p.pos, p.src);
   return hipGetLastError();
 }
+
+#ifdef MOE_CHECKED
+hipError_t oob_counter_plan(unsigned int** p) { return oob_counter_address(p); }
+#endif
 
 }  // namespace moe

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void moe_permute(const uint4* __restrict__ x,
     const uint4 v0 = xr[c], v1 = xr[c + 64], v2 = xr[c + 128], v3 = xr[c + 192];
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
-      if (p < 0) continue;
+      if (p < 0 || !MOE_CHECK(p < T * K)) continue;
       uint4* dst = xg + (int64_t)p * nch + c;
       dst[0] = v0; dst[64] = v1; dst[128] = v2; dst[192] = v3;
     }
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void moe_permute(const uint4* __restrict__ x,
     const uint4 v = xr[c];
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
-      if (p >= 0) xg[(int64_t)p * nch + c] = v;
+      if (p >= 0 && MOE_CHECK(p < T * K)) xg[(int64_t)p * nch + c] = v;
     }
   }
 }
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void moe_combine(const uint4* __restrict__ row
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       pk[k] = pt[k];
+      if (pk[k] >= 0 && !MOE_CHECK(pk[k] < T * K)) pk[k] = -1;
       wk[k] = WEIGHTED ? st[k] : 1.0f;
     }
     for (; c + 64 < nch; c += 128) {
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void moe_combine(const uint4* __restrict__ row
       float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, a1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int k = 0; k < K; ++k) {
         const int p = pt[k];
-        if (p < 0) continue;
+        if (p < 0 || !MOE_CHECK(p < T * K)) continue;
         const float w = WEIGHTED ? st[k] : 1.0f;
         const uint4* r = rows + (int64_t)p * nch + c;
         const uint4 v0 = load_once(r), v1 = load_once(r + 64);
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256) void moe_combine(const uint4* __restrict__ row
     float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
-      if (p < 0) continue;
+      if (p < 0 || !MOE_CHECK(p < T * K)) continue;
       const float w = WEIGHTED ? st[k] : 1.0f;
       float f0[8];
       unpack8(load_once(rows + (int64_t)p * nch + c), f0);
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_dscores(const uint4* __re
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       pk[j] = pos[(int64_t)t * KT + j];
+      if (pk[j] >= 0 && !MOE_CHECK(pk[j] < T * K)) pk[j] = -1;
       sk[j] = scores[(int64_t)t * KT + j];
       part[j] = 0.0f;
     }
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_dscores(const uint4* __re
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       pk[j] = j < kn ? pos[(int64_t)t * K + k0 + j] : -1;
+      if (pk[j] >= 0 && !MOE_CHECK(pk[j] < T * K)) pk[j] = -1;
       sk[j] = j < kn ? scores[(int64_t)t * K + k0 + j] : 0.0f;
       part[j] = 0.0f;
     }
@@ -298,5 +301,9 @@ hipError_t launch_combine_bwd(const moe_shape& s, const int32_t* pos, const uint
   }
   return hipGetLastError();
 }
+
+#ifdef MOE_CHECKED
+hipError_t oob_counter_rowops(unsigned int** p) { return oob_counter_address(p); }
+#endif
 
 }  // namespace moe

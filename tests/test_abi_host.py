@@ -50,6 +50,26 @@ def test_library_exports_every_declared_function():
     assert set(M.EXPORTED) == set(names)
 
 
+def test_checked_library_exports_the_same_entry_points_and_its_own():
+    """libmoe_routed_checked.so exports every entry point of moe_routed.h plus those of
+    moe_routed_checked.h; the product library exports none of the latter."""
+    checked = os.path.join(ROOT, "mixture_experts_routed_plan_amd", "libmoe_routed_checked.so")
+    if not os.path.exists(checked):
+        _load_build_script(ROOT).build()
+    text = open(os.path.join(ROOT, "include", "moe_routed_checked.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    own = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    assert own == {"moe_checked_violations", "moe_checked_reset", "moe_checked_shrink"}
+
+    def exported(path):
+        nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                            text=True).stdout
+        return set(re.findall(r"\bT (moe_\w+)", nm))
+
+    assert exported(checked) == set(declared_functions()) | own
+    assert not (exported(LIB) & own)
+
+
 def test_abi_version_and_status_strings():
     assert M.moe_abi_version() == 4
     for st in range(0, -9, -1):
