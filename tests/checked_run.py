@@ -6,8 +6,9 @@ For each shape (ragged, skewed with an empty expert, one token, 1024 experts wit
 expert, K=6) and every flag combination (saving or not, recompute, xg kept, weight gradients in
 bf16 or fp32, overwritten or accumulated): plan, forward, backward (when saving) or the
 allocation-free forward, and the three row steps as entry points; after each, the violation
-count of the checked kernels must be zero. The default-flag results are also held to the
-oracle's elementwise bar, so the checks change nothing in what is computed. Finally the checks
+count of the checked kernels must be zero. The same at the four full-size workloads and with x
+just under 4 GiB. The default-flag results at the small shapes are also held to the oracle's
+elementwise bar, so the checks change nothing in what is computed. Finally the checks
 themselves: with every GEMM extent taken 16 bytes short, a forward must report violations.
 """
 import itertools
@@ -129,6 +130,26 @@ def checks_detect():
     log("[checks] extents 16 bytes short: %d violations reported; restored: none" % n)
 
 
+def run_large(name, w):
+    """A full-size workload (default flags and fp32 weight-gradient accumulation): plan,
+    forward, backward with no access outside a buffer."""
+    inp = W.make_inputs(w, with_dout=True, router=oracle.route)
+    x, w13, w2, dout = (dv.to_device_bits(a) for a in (inp.x, inp.w13, inp.w2, inp.dout))
+    ids = torch.from_numpy(inp.ids).cuda()
+    scores = torch.from_numpy(inp.scores).cuda()
+    for acc_f32 in (False, True):
+        layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, wgrad_accumulate=acc_f32, wgrad_f32=acc_f32)
+        layer.plan(ids)
+        layer.forward(x, scores, w13, w2)
+        layer.backward(dout, scores, w13, w2)
+        torch.cuda.synchronize()
+        violations("%s accumulate/f32=%d" % (name, acc_f32))
+        del layer
+    del x, w13, w2, dout, ids, scores, inp
+    torch.cuda.empty_cache()
+    log("[%s] full size: no access outside a buffer" % name)
+
+
 def main():
     assert M.CHECKED, "set MOE_ROUTED_LIBRARY=checked"
     assert torch.cuda.is_available()
@@ -136,6 +157,11 @@ def main():
     for name, w in SHAPES.items():
         log("[%s] start" % name)
         run_shape(name, w)
+    for name in ("fine_grained", "large_hidden", "imbalanced", "training"):
+        run_large(name, W.WORKLOADS[name])
+    # x just under 4 GiB: the gate/up GEMM gathers token rows up to the end of x
+    run_large("x_below_4gib", W.Workload("x_below_4gib", T=2**20 - 1, D=2048, F=64, E=8, K=1,
+                                         routing="uniform_distinct", backward=True, seed=12))
     checks_detect()
     log("checked library: all cases clean")
 

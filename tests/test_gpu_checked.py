@@ -1,7 +1,7 @@
 """GPU: the checked library (libmoe_routed_checked.so, include/moe_routed_checked.h), whose kernels
 test every global memory access against its buffer, runs every shape and flag combination of the
-guard-region test, the allocation-free forward and the row steps without a single access outside
-a buffer, matches the oracle on the default flags, and reports violations when its extents are
+guard-region test, the allocation-free forward, the row steps, the four full-size workloads and
+x just under 4 GiB without a single access outside a buffer, matches the oracle on the default flags, and reports violations when its extents are
 taken 16 bytes short. The cases run in one child process (tests/checked_run.py), because the
 binding chooses its library once per process."""
 import os
