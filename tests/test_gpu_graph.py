@@ -1,0 +1,134 @@
+"""GPU: the hot path under HIP graph capture (Dist-MoE, "Use graph and checkpoint features": the
+layer is captured into a graph and replayed; the library's calls are sync-free, allocate nothing
+and launch a sequence whose grids depend on the shape only).
+
+plan + forward + backward are captured once (torch's graph capture, so the library launches on
+the capture stream) and replayed several times. Before each replay the outputs are cleared by
+eager work on the device, and eager work and synchronizations run between the replays; every
+replay must give bitwise the eager results. Replays after new values are copied into the same
+input buffers (x, ids, scores, weights, dout) must give bitwise the eager results for the new
+inputs, so the graph reads its inputs at replay time and keeps nothing from the capture. The
+weight gradients
+are also captured in the accumulating fp32 mode, where each replay adds onto what the previous
+left, and the result of n replays must equal n eager backward calls."""
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_check import log
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "p_ragged": W.PARITY_WORKLOADS["p_ragged"],
+    "p_skew": W.PARITY_WORKLOADS["p_skew"],
+    "fine_grained": W.WORKLOADS["fine_grained"],
+}
+
+
+def _dv():
+    from mixture_experts_routed_plan_amd import device as dv
+    return dv
+
+
+def _inputs(w, seed_shift=0):
+    dv = _dv()
+    inp = W.make_inputs(w.with_(seed=w.seed + seed_shift), with_dout=True, router=oracle.route)
+    return dict(x=dv.to_device_bits(inp.x), w13=dv.to_device_bits(inp.w13),
+                w2=dv.to_device_bits(inp.w2), dout=dv.to_device_bits(inp.dout),
+                ids=torch.from_numpy(inp.ids).cuda(), scores=torch.from_numpy(inp.scores).cuda())
+
+
+def _step(layer, d):
+    layer.plan(d["ids"])
+    layer.forward(d["x"], d["scores"], d["w13"], d["w2"])
+    layer.backward(d["dout"], d["scores"], d["w13"], d["w2"])
+
+
+def _outputs(layer):
+    return [t.clone() for t in (layer.out, layer.dx, layer.dscores, layer.dw13, layer.dw2)]
+
+
+def _clear(layer):
+    for t in (layer.out, layer.dx, layer.dscores, layer.dw13, layer.dw2):
+        t.fill_(float("nan"))
+
+
+def _capture(layer, d):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(layer, d)  # warm-up on the capture stream's side, as torch recommends
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _step(layer, d)
+    torch.cuda.synchronize()
+    return g
+
+
+def _same(a, b, what):
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32)), \
+            "%s: output %d differs" % (what, i)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_captured_step_replays_bitwise(name):
+    dv = _dv()
+    w = CASES[name]
+    d = _inputs(w)
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K)
+    _step(layer, d)
+    torch.cuda.synchronize()
+    ref = _outputs(layer)
+    g = _capture(layer, d)
+    noise = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        _clear(layer)
+        noise.mul_(1.0001).add_(0.5)  # unrelated eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(_outputs(layer), ref, "%s replay %d" % (name, rep))
+    # new inputs copied into the captured buffers
+    d2 = _inputs(w, seed_shift=100)
+    for k in d:
+        d[k].copy_(d2[k])
+    torch.cuda.synchronize()
+    fresh = dv.Layer(w.T, w.D, w.F, w.E, w.K)
+    _step(fresh, d2)
+    torch.cuda.synchronize()
+    ref2 = _outputs(fresh)
+    for rep in range(2):
+        _clear(layer)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(_outputs(layer), ref2, "%s new inputs, replay %d" % (name, rep))
+    log("[%s] 6 replays bitwise equal to the eager calls, new inputs picked up" % name)
+
+
+def test_captured_accumulating_weight_gradients():
+    dv = _dv()
+    w = CASES["p_ragged"]
+    d = _inputs(w)
+    eager = dv.Layer(w.T, w.D, w.F, w.E, w.K, wgrad_accumulate=True, wgrad_f32=True)
+    for _ in range(3):
+        _step(eager, d)
+    torch.cuda.synchronize()
+    ref = [eager.dw13.clone(), eager.dw2.clone()]
+    layer = dv.Layer(w.T, w.D, w.F, w.E, w.K, wgrad_accumulate=True, wgrad_f32=True)
+    g = _capture(layer, d)  # the warm-up accumulated once (a capture runs nothing): start over
+    layer.dw13.zero_()
+    layer.dw2.zero_()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+    assert torch.equal(layer.dw13.view(torch.int32), ref[0].view(torch.int32))
+    assert torch.equal(layer.dw2.view(torch.int32), ref[1].view(torch.int32))
+    log("[p_ragged] 3 accumulating replays bitwise equal to 3 eager backward calls")
