@@ -1,4 +1,4 @@
-"""GPU: the hot path under HIP graph capture (Dist-MoE, "Use graph and checkpoint features": the
+"""GPU: the hot path under HIP graph capture and on concurrent streams (Dist-MoE, "Use graph and checkpoint features": the
 layer is captured into a graph and replayed; the library's calls are sync-free, allocate nothing
 and launch a sequence whose grids depend on the shape only).
 
@@ -132,3 +132,32 @@ def test_captured_accumulating_weight_gradients():
     assert torch.equal(layer.dw13.view(torch.int32), ref[0].view(torch.int32))
     assert torch.equal(layer.dw2.view(torch.int32), ref[1].view(torch.int32))
     log("[p_ragged] 3 accumulating replays bitwise equal to 3 eager backward calls")
+
+
+def test_two_layers_on_two_streams_concurrently():
+    """The library keeps no state between calls and launches only on the stream it is given: two
+    layers with different inputs, each queued whole on its own stream with no synchronization
+    between them, give bitwise their results from a single stream."""
+    dv = _dv()
+    ws = [CASES["p_ragged"], CASES["p_skew"]]
+    ds = [_inputs(w) for w in ws]
+    refs = []
+    for w, d in zip(ws, ds):
+        layer = dv.Layer(w.T, w.D, w.F, w.E, w.K)
+        _step(layer, d)
+        torch.cuda.synchronize()
+        refs.append(_outputs(layer))
+    layers = [dv.Layer(w.T, w.D, w.F, w.E, w.K) for w in ws]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for layer in layers:
+            _clear(layer)
+        torch.cuda.synchronize()
+        for layer, d, st in zip(layers, ds, streams):
+            with torch.cuda.stream(st):
+                _step(layer, d)
+        torch.cuda.synchronize()
+        for i, layer in enumerate(layers):
+            _same(_outputs(layer), refs[i], "stream %d, round %d" % (i, rep))
+    log("two layers on two streams: bitwise their single-stream results")
