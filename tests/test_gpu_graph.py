@@ -1,6 +1,6 @@
-"""GPU: the hot path under HIP graph capture and on concurrent streams (Dist-MoE, "Use graph and checkpoint features": the
-layer is captured into a graph and replayed; the library's calls are sync-free, allocate nothing
-and launch a sequence whose grids depend on the shape only).
+"""GPU: the hot path under HIP graph capture and on concurrent streams (Dist-MoE, "Use graph and
+checkpoint features": the layer is captured into a graph and replayed; the library's calls are
+sync-free, allocate nothing and launch a sequence whose grids depend on the shape only).
 
 plan + forward + backward are captured once (torch's graph capture, so the library launches on
 the capture stream) and replayed several times. Before each replay the outputs are cleared by
